@@ -1,0 +1,196 @@
+"""Benchmark: GiB/s written by the counter-based bulk fills on one MI355X.
+
+One step runs every fill of the hot path once at 2^28 elements (tandem-cuda,
+"Performance", §GPU: 2^28 elements into device memory): the uniform fills (u8, u16,
+f16 bits, u32, u64, f32, f64, bool; key and start draw cycle through 1..3 and 0, 1, 3
+from step to step), the bounded fills (u32/u64 below 1000 and below 2^W - 2, int32 and
+int64 with a low bound), the f64 ziggurat and f32 Box-Muller normals, fused dropout over
+X = f32[2^20, 256] (p = 0.1), the choice fill through a 1000-way Zipf(1.1) alias table,
+and the Philox4x32-10 u32 fill.  Inputs are resident in device memory before timing.
+
+The JSON line reports the whole step's bytes written per second (`value`), each fill's
+median rate, the roofline of the dominant kernel (algorithmic bytes per launch over its
+HIP-event-timed average duration, against the 8 TB/s HBM peak), and the CPU oracle timed
+on a bounded sample of the same step on this host.
+"""
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+
+GIB = float(1 << 30)
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup-seconds", type=float, default=2.0,
+                    help="keep warming up for at least this long (the pages warm each row for 2 s)")
+    ap.add_argument("--cpu-sample-log2", type=int, default=22,
+                    help="elements per fill in the oracle's CPU sample (0 disables it)")
+    ap.add_argument("--only", default="", help="comma-separated fill names to run (profiling)")
+    return ap.parse_args()
+
+
+def build_step(tk, torch, n):
+    """Returns a list of (name, bytes_written, bytes_read, kernels, fn(step_index))."""
+    import tk_inputs as ti
+    dev = torch.device("cuda")
+    out = torch.empty(8 * n, dtype=torch.uint8, device=dev)   # 2 GiB, reused by every fill
+    x = torch.empty(n, dtype=torch.float32, device=dev)       # dropout input
+    tk.tk_fill_normal_f32(ti.DROPOUT_X_KEY, 0, n, x)          # X ~ N(0, 1), seed 7
+    table = tk.tk_alias_create(ti.zipf_weights())
+    optr = out.data_ptr()
+    ks = lambda s: ti.KEYS[s % 3]
+    st = lambda s: ti.STARTS[s % 3]
+    fills = [
+        ("u32", 4 * n, 0, 1, lambda s: tk.tk_fill_u32(ks(s), st(s), n, optr)),
+        ("u64", 8 * n, 0, 1, lambda s: tk.tk_fill_u64(ks(s), st(s), n, optr)),
+        ("f32", 4 * n, 0, 1, lambda s: tk.tk_fill_f32(ks(s), st(s), n, optr)),
+        ("f64", 8 * n, 0, 1, lambda s: tk.tk_fill_f64(ks(s), st(s), n, optr)),
+        ("u16", 2 * n, 0, 1, lambda s: tk.tk_fill_u16(ks(s), st(s), n, optr)),
+        ("f16_bits", 2 * n, 0, 1, lambda s: tk.tk_fill_f16_bits(ks(s), st(s), n, optr)),
+        ("u8", n, 0, 1, lambda s: tk.tk_fill_u8(ks(s), st(s), n, optr)),
+        ("bool", n, 0, 1, lambda s: tk.tk_fill_bool(ks(s), st(s), n, optr)),
+        ("u32_below_1000", 4 * n, 0, 1, lambda s: tk.tk_fill_u32_below(1, 0, n, 1000, optr)),
+        ("u32_below_2^32-2", 4 * n, 0, 1, lambda s: tk.tk_fill_u32_below(1, 0, n, (1 << 32) - 2, optr)),
+        ("u64_below_1000", 8 * n, 0, 1, lambda s: tk.tk_fill_u64_below(1, 0, n, 1000, optr)),
+        ("u64_below_2^64-2", 8 * n, 0, 1, lambda s: tk.tk_fill_u64_below(1, 0, n, (1 << 64) - 2, optr)),
+        ("i32_below_low", 4 * n, 0, 1, lambda s: tk.tk_fill_i32_below(1, 0, n, ti.LOW, ti.LOW_BOUND, optr)),
+        ("i64_below32_low", 8 * n, 0, 1, lambda s: tk.tk_fill_i64_below32(1, 0, n, ti.LOW, ti.LOW_BOUND, optr)),
+        ("normal_f64", 8 * n, 0, 2, lambda s: tk.tk_fill_normal_f64(1, st(s), n, optr)),
+        ("normal_f32", 4 * n, 0, 1, lambda s: tk.tk_fill_normal_f32(1, 0, n, optr)),
+        ("dropout_f32", 4 * n, 4 * n, 1,
+         lambda s: tk.tk_dropout_f32(ti.DROPOUT_KEY, 0, n, ti.DROPOUT_P, x.data_ptr(), optr)),
+        ("choice_u32", 4 * n, 0, 1, lambda s: tk.tk_fill_choice_u32(1, 0, n, table, optr)),
+        ("philox_u32", 4 * n, 0, 1, lambda s: tk.tk_philox_fill_u32(1, st(s), n, optr)),
+    ]
+    return fills, (out, x, table)
+
+
+def cpu_baseline(n_sample):
+    """The oracle (single-threaded C) over the same fills at n_sample elements each."""
+    import oracle
+    import tk_inputs as ti
+    x = ti.normal_x(n_sample)
+    q, a, _ = oracle.alias_build(ti.zipf_weights())
+    m = n_sample
+    jobs = [
+        (4 * m, lambda: oracle.fill_u32(1, 0, m)), (8 * m, lambda: oracle.fill_u64(1, 0, m)),
+        (4 * m, lambda: oracle.fill_f32(1, 0, m)), (8 * m, lambda: oracle.fill_f64(1, 0, m)),
+        (2 * m, lambda: oracle.fill_u16(1, 0, m)), (2 * m, lambda: oracle.fill_f16_bits(1, 0, m)),
+        (m, lambda: oracle.fill_u8(1, 0, m)), (m, lambda: oracle.fill_bool(1, 0, m)),
+        (4 * m, lambda: oracle.fill_u32_below(1, 0, m, 1000)),
+        (4 * m, lambda: oracle.fill_u32_below(1, 0, m, (1 << 32) - 2)),
+        (8 * m, lambda: oracle.fill_u64_below(1, 0, m, 1000)),
+        (8 * m, lambda: oracle.fill_u64_below(1, 0, m, (1 << 64) - 2)),
+        (4 * m, lambda: oracle.fill_i32_below(1, 0, m, ti.LOW, ti.LOW_BOUND)),
+        (8 * m, lambda: oracle.fill_i64_below32(1, 0, m, ti.LOW, ti.LOW_BOUND)),
+        (8 * m, lambda: oracle.fill_normal_f64(1, 0, m)), (4 * m, lambda: oracle.fill_normal_f32(1, 0, m)),
+        (4 * m, lambda: oracle.dropout_f32(ti.DROPOUT_KEY, 0, x, ti.DROPOUT_P, with_mask=False)),
+        (4 * m, lambda: oracle.fill_choice_u32(1, 0, m, q, a)), (4 * m, lambda: oracle.philox_fill_u32(1, 0, m)),
+    ]
+    total_bytes, total_s = 0, 0.0
+    for nbytes, fn in jobs:
+        t0 = time.perf_counter()
+        fn()
+        total_s += time.perf_counter() - t0
+        total_bytes += nbytes
+    return {"value": total_bytes / total_s / GIB, "unit": "GiB/s", "cores": 1, "kind": "oracle",
+            "sample": f"every fill of one step at 2^{int(np.log2(n_sample))} elements instead of 2^28 "
+                      f"(single-threaded C oracle, {total_s:.1f} s)"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the fills shard with no communication, so only "
+              "--gpus 1 is supported here", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import bulk_fills_amd as tk
+    import tk_inputs as ti
+
+    n = ti.FULL_N
+    fills, keep = build_step(tk, torch, n)
+    if args.only:
+        wanted = set(args.only.split(","))
+        fills = [f for f in fills if f[0] in wanted]
+    torch.cuda.synchronize()
+
+    def step(s, events=None):
+        for j, (_, _, _, _, fn) in enumerate(fills):
+            if events is not None:
+                events[j][0].record()
+            fn(s)
+            if events is not None:
+                events[j][1].record()
+
+    t_end = time.perf_counter() + args.warmup_seconds
+    w = 0
+    while w < args.warmup or time.perf_counter() < t_end:
+        step(w)
+        w += 1
+        if w % 10 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    evs = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in fills]
+           for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(K):
+        step(s, evs[s])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+
+    elapsed = t1 - t0
+    bytes_step = sum(f[1] for f in fills)
+    value = bytes_step * K / elapsed / GIB
+    per_fill = {}
+    for j, (name, wbytes, rbytes, nk, _) in enumerate(fills):
+        ms = [evs[s][j][0].elapsed_time(evs[s][j][1]) for s in range(K)]
+        per_fill[name] = {"median_ms": statistics.median(ms), "mean_ms": statistics.fmean(ms),
+                          "min_ms": min(ms), "GiB_per_s": wbytes / (statistics.median(ms) / 1e3) / GIB,
+                          "bytes_written": wbytes, "bytes_read": rbytes, "kernels": nk}
+    # dominant single-kernel fill: the largest share of the step's device time
+    single = {k: v for k, v in per_fill.items() if v["kernels"] == 1}
+    dom = max(single, key=lambda k: single[k]["mean_ms"])
+    d = per_fill[dom]
+    algo_bytes = d["bytes_written"] + d["bytes_read"]
+    achieved = algo_bytes / (d["mean_ms"] / 1e3) / 1e9
+    roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "bytes_per_launch": algo_bytes, "avg_launch_ms": round(d["mean_ms"], 5)}
+    cpu = cpu_baseline(1 << args.cpu_sample_log2) if args.cpu_sample_log2 > 0 else None
+
+    rec = {
+        "metric": "GiB/s written per fill (2^28 elems) on 1 MI355X; % of HBM write peak",
+        "value": round(value, 2), "unit": "GiB/s", "n_gpus": 1, "steps": K, "warmup": w,
+        "ms_per_step": round(elapsed / K * 1e3, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "u32", "data": "synthetic",
+        "config": {"workload": "every hot-path fill once per step at 2^28 elements: uniform u8/u16/f16/u32/u64/"
+                               "f32/f64/bool, bounded (Lemire) x6, ziggurat f64 normal, Box-Muller f32 normal, "
+                               "dropout over f32[2^20,256], Zipf(1.1)x1000 choice, Philox u32",
+                   "elements_per_fill": n, "fills_per_step": len(fills), "bytes_written_per_step": bytes_step},
+        "pct_of_hbm_peak": round(100 * value * GIB / 1e9 / HBM_PEAK_GBS, 2),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "fills": {k: {"GiB_per_s": round(v["GiB_per_s"], 1), "median_ms": round(v["median_ms"], 4),
+                      "min_ms": round(v["min_ms"], 4)} for k, v in per_fill.items()},
+        "device": torch.cuda.get_device_name(0),
+    }
+    print(json.dumps(rec), flush=True)
+    del keep
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,235 @@
+// tk_choice.hip -- weighted choice through an alias table.
+//
+// tandem-sycl, "Design", §Fills: the choice fill maps each 64-bit draw through an alias
+// table.  The table is built once on the host (Vose's method in integers, so it is exact
+// and reproducible) and uploaded as n pairs {q, alias}.  The fill keeps the table in LDS
+// (one copy per work-group of a persistent grid) and maps draw d to column
+// c = (hi32(d) n) >> 32, coin lo32(d): out = coin < q[c] ? c : alias[c].  Four indices
+// leave as one 16-byte store.
+#include <math.h>
+
+#include <deque>
+#include <vector>
+
+#include "tk_device.h"
+#include "tk_internal.h"
+
+struct tk_alias {
+  int device;
+  uint32_t n;
+  uint2 *table;  // device: {q, alias} per column
+  std::vector<uint32_t> q, alias;
+};
+
+namespace tk {
+
+constexpr uint32_t kChoiceLdsMax = 8192;  // columns kept in LDS (64 KiB); larger tables are read from L2
+constexpr int kChoiceUnroll = 2;
+
+// Vose's alias construction over integer masses.  Index j owns
+// m_j = floor(w_j / S * n 2^32) of the n 2^32 total; the rounding remainder goes to the
+// largest weight (first on ties).  Columns are filled from two FIFO lists in index order:
+// an under-full index takes the front over-full one as its alias, which gives up the
+// difference and rejoins the under-full list once below 2^32.
+static bool build_alias(const double *w, uint32_t n, std::vector<uint32_t> &q, std::vector<uint32_t> &alias) {
+  double total_w = 0.0;
+  for (uint32_t j = 0; j < n; ++j) {
+    if (!(w[j] >= 0.0) || !std::isfinite(w[j])) return false;
+    total_w += w[j];
+  }
+  if (!(total_w > 0.0) || !std::isfinite(total_w)) return false;
+  const uint64_t full = 1ull << 32;
+  const uint64_t total = (uint64_t)n << 32;
+  std::vector<uint64_t> mass(n);
+  uint64_t assigned = 0;
+  uint32_t biggest = 0;
+  for (uint32_t j = 0; j < n; ++j) {
+    mass[j] = (uint64_t)std::floor(w[j] / total_w * (double)total);
+    assigned += mass[j];
+    if (w[j] > w[biggest]) biggest = j;
+  }
+  mass[biggest] = (uint64_t)((int64_t)mass[biggest] + ((int64_t)total - (int64_t)assigned));
+  q.assign(n, 0);
+  alias.resize(n);
+  std::deque<uint32_t> under, over;
+  for (uint32_t j = 0; j < n; ++j) (mass[j] < full ? under : over).push_back(j);
+  while (!under.empty() && !over.empty()) {
+    const uint32_t s = under.front();
+    under.pop_front();
+    const uint32_t l = over.front();
+    q[s] = (uint32_t)mass[s];
+    alias[s] = l;
+    mass[l] -= full - mass[s];
+    if (mass[l] < full) {
+      over.pop_front();
+      under.push_back(l);
+    }
+  }
+  for (uint32_t j : over) { q[j] = 0; alias[j] = j; }   // exactly full columns
+  for (uint32_t j : under) { q[j] = 0; alias[j] = j; }  // unreachable with exact masses
+  return true;
+}
+
+struct ChoiceArgs {
+  uint32_t *out;
+  uint64_t start, head, nvec;
+  uint32_t tail;
+  uint32_t hk;
+  uint32_t n;
+  const uint2 *table;
+};
+
+template <bool kLds>
+__device__ __forceinline__ uint32_t choose(const ChoiceArgs &a, const uint2 *tab, uint32_t lo, uint32_t hi) {
+  const uint32_t col = __umulhi(hi, a.n);
+  const uint2 e = kLds ? tab[col] : a.table[col];
+  return lo < e.x ? col : e.y;
+}
+
+template <bool kLds>
+__device__ __forceinline__ uint32_t choice_elem(const ChoiceArgs &a, const uint2 *tab, uint64_t k) {
+  const uint32_t c = 2u * (uint32_t)(a.start + k);
+  return choose<kLds>(a, tab, word(a.hk, c), word(a.hk, c + 1));
+}
+
+template <int U, bool kLds, bool kNT>
+__global__ __launch_bounds__(kBlock) void k_choice(ChoiceArgs a, uint64_t ntiles) {
+  extern __shared__ uint2 tab[];
+  if (kLds) {
+    for (uint32_t i = threadIdx.x; i < a.n; i += kBlock) tab[i] = a.table[i];
+    __syncthreads();
+  }
+  for (uint64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+    const uint64_t v0 = tile * (uint64_t)(kBlock * U) + threadIdx.x;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint64_t v = v0 + (uint64_t)u * kBlock;
+      if (v >= a.nvec) continue;
+      const uint32_t c = 2u * (uint32_t)(a.start + a.head + 4 * v);
+      uint32_t r[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) r[j] = choose<kLds>(a, tab, word(a.hk, c + 2 * j), word(a.hk, c + 2 * j + 1));
+      store16<kNT>(a.out + a.head + 4 * v, make_uint4(r[0], r[1], r[2], r[3]));
+    }
+  }
+  if (blockIdx.x == 0) {
+    const uint32_t t = threadIdx.x;
+    if (t < a.head) a.out[t] = choice_elem<kLds>(a, tab, t);
+    if (t >= 128 && t - 128 < a.tail) {
+      const uint64_t k = a.head + 4 * a.nvec + (t - 128);
+      a.out[k] = choice_elem<kLds>(a, tab, k);
+    }
+  }
+}
+
+template <bool kLds>
+static void launch_choice(const ChoiceArgs &a, uint32_t grid, uint64_t ntiles, hipStream_t stream) {
+  const size_t lds = kLds ? (size_t)a.n * sizeof(uint2) : 0;
+  if (config().nt_stores)
+    hipLaunchKernelGGL((k_choice<kChoiceUnroll, kLds, true>), dim3(grid), dim3(kBlock), lds, stream, a, ntiles);
+  else
+    hipLaunchKernelGGL((k_choice<kChoiceUnroll, kLds, false>), dim3(grid), dim3(kBlock), lds, stream, a, ntiles);
+}
+
+}  // namespace tk
+
+using namespace tk;
+
+extern "C" {
+
+tk_status tk_alias_create(const double *weights, uint32_t n, tk_alias **table) {
+  if (!weights || !table || n == 0 || n > (1u << 24)) return TK_EINVAL;
+  *table = nullptr;
+  tk_alias *t = new tk_alias();
+  t->n = n;
+  t->table = nullptr;
+  if (!build_alias(weights, n, t->q, t->alias)) {  // weights are checked before any HIP call
+    delete t;
+    return TK_EINVAL;
+  }
+  tk_status st;
+  const int dev = current_device(&st);
+  if (dev < 0) {
+    delete t;
+    return st;
+  }
+  t->device = dev;
+  std::vector<uint2> packed(n);
+  for (uint32_t j = 0; j < n; ++j) packed[j] = make_uint2(t->q[j], t->alias[j]);
+  if (hipMalloc(&t->table, n * sizeof(uint2)) != hipSuccess) {
+    delete t;
+    return TK_ENOMEM;
+  }
+  if ((st = hip_status(hipMemcpy(t->table, packed.data(), n * sizeof(uint2), hipMemcpyHostToDevice))) != TK_OK) {
+    (void)hipFree(t->table);
+    delete t;
+    return st;
+  }
+  *table = t;
+  return TK_OK;
+}
+
+tk_status tk_alias_destroy(tk_alias *t) {
+  if (!t) return TK_EINVAL;
+  tk_status st = TK_OK;
+  if (t->table) st = hip_status(hipFree(t->table));
+  delete t;
+  return st;
+}
+
+uint32_t tk_alias_size(const tk_alias *t) { return t ? t->n : 0; }
+
+tk_status tk_alias_build_host(const double *weights, uint32_t n, uint32_t *q, uint32_t *alias) {
+  if (!weights || !q || !alias || n == 0 || n > (1u << 24)) return TK_EINVAL;
+  std::vector<uint32_t> vq, va;
+  if (!build_alias(weights, n, vq, va)) return TK_EINVAL;
+  for (uint32_t j = 0; j < n; ++j) {
+    q[j] = vq[j];
+    alias[j] = va[j];
+  }
+  return TK_OK;
+}
+
+tk_status tk_alias_export(const tk_alias *t, uint32_t *q, uint32_t *alias) {
+  if (!t || !q || !alias) return TK_EINVAL;
+  for (uint32_t j = 0; j < t->n; ++j) {
+    q[j] = t->q[j];
+    alias[j] = t->alias[j];
+  }
+  return TK_OK;
+}
+
+tk_status tk_fill_choice_u32(uint32_t key, uint64_t start_draw, uint64_t n, const tk_alias *table, uint32_t *out,
+                             hipStream_t stream) {
+  if (!table) return TK_EINVAL;
+  if (n == 0) return TK_OK;
+  if (!out || ((uintptr_t)out & 3u)) return TK_EINVAL;
+  if (start_draw > 0x7FFFFFFFull || n - 1 > 0x7FFFFFFFull - start_draw) return TK_ERANGE;
+  tk_status st;
+  const int dev = current_device(&st);
+  if (dev < 0) return st;
+  if (dev != table->device) return TK_EINVAL;
+
+  ChoiceArgs a{};
+  a.out = out;
+  a.start = start_draw;
+  const uint64_t mis = (uintptr_t)out & 15u;
+  a.head = mis ? (16 - mis) / 4 : 0;
+  if (a.head > n) a.head = n;
+  a.nvec = (n - a.head) / 4;
+  a.tail = (uint32_t)(n - a.head - 4 * a.nvec);
+  a.hk = host_lowbias32(key);
+  a.n = table->n;
+  a.table = table->table;
+
+  const uint64_t per_tile = (uint64_t)kBlock * kChoiceUnroll;
+  const uint64_t ntiles = (a.nvec + per_tile - 1) / per_tile;
+  uint64_t grid = (uint64_t)device_cus(dev) * (uint64_t)config().choice_blocks_per_cu;
+  if (grid > ntiles) grid = ntiles;
+  if (grid == 0) grid = 1;
+  if (a.n <= kChoiceLdsMax) launch_choice<true>(a, (uint32_t)grid, ntiles, stream);
+  else launch_choice<false>(a, (uint32_t)grid, ntiles, stream);
+  return launch_status();
+}
+
+}  // extern "C"

@@ -1,0 +1,179 @@
+// tk_device.h -- device-side generator and transforms for gfx950 (wave64).
+//
+// Everything here is inline __device__ code used by the fill kernels.  Integer work is
+// exact; floating-point transforms are either exact (uniform grids, the ziggurat fast
+// path) or evaluated as single IEEE operations with contraction disabled at build time
+// (-ffp-contract=off), so results match a plain CPU evaluation bit for bit.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tk {
+
+constexpr int kBlock = 256;  // work-group size: four wave64s
+
+// ---- lowbias32 (Phobos stdlib, "Random numbers", §hash32) -----------------------------
+// Three logical xorshifts and two wrapping 32-bit multiplies; the multipliers are the
+// page's i32 constants 2146121005 and -2073254261 as u32 bit patterns.
+__device__ __forceinline__ uint32_t lowbias32(uint32_t x) {
+  x ^= x >> 16;
+  x *= 0x7FEB352Du;
+  x ^= x >> 15;
+  x *= 0x846CA68Bu;
+  x ^= x >> 16;
+  return x;
+}
+
+// Word c of the stream keyed by hk = lowbias32(key) (Phobos, §uniform: counter ^ hash(seed)).
+__device__ __forceinline__ uint32_t word(uint32_t hk, uint32_t c) { return lowbias32(c ^ hk); }
+
+// ---- exact uniform transforms ---------------------------------------------------------
+// f32: (w & 0x7FFFFF) * 2^-23 built as the float 1.m minus 1 (exact: both are on the
+// 2^-23 grid of [1, 2)).
+__device__ __forceinline__ float unit23(uint32_t w) {
+  return __uint_as_float((w & 0x7FFFFFu) | 0x3F800000u) - 1.0f;
+}
+
+// f64: (d & (2^53-1)) * 2^-53 from the two words: hi's low 21 bits scaled by 2^-21 plus
+// lo scaled by 2^-53.  Both terms and their sum are exact.
+__device__ __forceinline__ double unit53_lowbits(uint32_t lo, uint32_t hi) {
+  return (double)(hi & 0x1FFFFFu) * 0x1p-21 + (double)lo * 0x1p-53;
+}
+
+// (d >> 11) * 2^-53 for the ziggurat: the top 53 bits of the draw.
+__device__ __forceinline__ double unit53_topbits(uint32_t lo, uint32_t hi) {
+  return (double)hi * 0x1p-32 + (double)(lo >> 11) * 0x1p-53;
+}
+
+// Two binary16 values (m & 0x7FF) * 2^-11 for the low and high halves of w, packed.  The
+// values are exact in binary16, so the round-toward-zero pack is exact.
+__device__ __forceinline__ uint32_t half_pair_bits(uint32_t w) {
+  float a = (float)(w & 0x7FFu) * 0x1p-11f;
+  float b = (float)((w >> 16) & 0x7FFu) * 0x1p-11f;
+  auto h = __builtin_amdgcn_cvt_pkrtz(a, b);
+  uint32_t bits;
+  __builtin_memcpy(&bits, &h, 4);
+  return bits;
+}
+
+// Four consecutive bits of `bits` starting at `shift`, one per byte (0 or 1).
+__device__ __forceinline__ uint32_t nibble_to_bytes(uint32_t bits, int shift) {
+  uint32_t nib = (bits >> shift) & 0xFu;
+  return (nib * 0x00204081u) & 0x01010101u;  // bit j moves to bit 8j
+}
+
+// ---- cross-lane hand-off ----------------------------------------------------------------
+__device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63u); }
+
+// The value held by the next lane of the wave (lane 63 receives lane 0's; callers replace
+// it).  Every lane of the wave must execute this.
+__device__ __forceinline__ uint32_t from_next_lane(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_ds_bpermute((lane_id() + 1) << 2, (int)v);
+}
+__device__ __forceinline__ float from_next_lane(float v) {
+  return __int_as_float(__builtin_amdgcn_ds_bpermute((lane_id() + 1) << 2, __float_as_int(v)));
+}
+
+// ---- substreams (tandem-sycl, "Design", §Normals: split(g) of sub(PURPOSE) of the key) --
+// The host passes hkp = lowbias32(sub(key, P)); the substream of draw g has key
+// split = word(hkp, g) and word j = word(lowbias32(split), j).
+struct Substream {
+  uint32_t hs;  // lowbias32 of the substream key
+  uint32_t pos; // next 32-bit word
+  __device__ __forceinline__ Substream(uint32_t hkp, uint32_t g) : hs(lowbias32(word(hkp, g))), pos(0) {}
+  __device__ __forceinline__ uint32_t next32() { return word(hs, pos++); }
+  __device__ __forceinline__ uint64_t next64() {
+    uint32_t lo = word(hs, pos), hi = word(hs, pos + 1);
+    pos += 2;
+    return (uint64_t)lo | ((uint64_t)hi << 32);
+  }
+};
+
+// Substream positions a rejection loop may consume before it stops; reaching it has
+// probability below 2^-65536.  The result is then defined: the last value for bounded
+// draws, NaN for normals.
+constexpr uint32_t kSubstreamCap = 65536u;
+
+// ---- Lemire multiply-shift with the exact threshold -----------------------------------
+// t = (2^W - s) mod s precomputed on the host; a draw is accepted when the low half of
+// x * s is at least t.
+__device__ __forceinline__ uint32_t lemire32(uint32_t x, uint32_t s, uint32_t t, uint32_t hkp, uint32_t g) {
+  uint64_t m = (uint64_t)x * s;
+  if (__builtin_expect((uint32_t)m < t, 0)) {
+    Substream ss(hkp, g);
+    for (uint32_t j = 0; j < kSubstreamCap; ++j) {
+      m = (uint64_t)ss.next32() * s;
+      if ((uint32_t)m >= t) break;
+    }
+  }
+  return (uint32_t)(m >> 32);
+}
+
+// 64 x 64 -> 128 multiply: returns the high half, low half in *lo.  When the bound fits
+// 32 bits (kSmall) two 32 x 64 products suffice.
+template <bool kSmall>
+__device__ __forceinline__ uint64_t mul_hi_lo(uint64_t x, uint64_t s, uint64_t *lo) {
+  if (kSmall) {
+    uint64_t p0 = (uint64_t)(uint32_t)x * (uint32_t)s;
+    uint64_t p1 = (x >> 32) * (uint32_t)s;
+    uint64_t mid = p1 + (p0 >> 32);
+    *lo = (mid << 32) | (uint32_t)p0;
+    return mid >> 32;
+  } else {
+    *lo = x * s;
+    return __umul64hi(x, s);
+  }
+}
+
+template <bool kSmall>
+__device__ __forceinline__ uint64_t lemire64(uint64_t x, uint64_t s, uint64_t t, uint32_t hkp, uint32_t g) {
+  uint64_t lo;
+  uint64_t hi = mul_hi_lo<kSmall>(x, s, &lo);
+  if (__builtin_expect(lo < t, 0)) {
+    Substream ss(hkp, g);
+    for (uint32_t j = 0; j < kSubstreamCap; ++j) {
+      hi = mul_hi_lo<kSmall>(ss.next64(), s, &lo);
+      if (lo >= t) break;
+    }
+  }
+  return hi;
+}
+
+// ---- Philox4x32-10 (Salmon et al., SC'11) ---------------------------------------------
+struct U32x4 {
+  uint32_t a, b, c, d;
+};
+
+__device__ __forceinline__ U32x4 philox4x32_10(uint64_t block, uint32_t k0, uint32_t k1) {
+  uint32_t c0 = (uint32_t)block, c1 = (uint32_t)(block >> 32), c2 = 0, c3 = 0;
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+    uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+    uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+    uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    c1 = (uint32_t)p1;
+    c3 = (uint32_t)p0;
+    c0 = n0;
+    c2 = n2;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return {c0, c1, c2, c3};
+}
+
+// ---- stores ----------------------------------------------------------------------------
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+template <bool kNT>
+__device__ __forceinline__ void store16(void *p, uint4 v) {
+  if (kNT) {
+    u32x4 w = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(w, (u32x4 *)p);
+  } else {
+    *(uint4 *)p = v;
+  }
+}
+
+}  // namespace tk

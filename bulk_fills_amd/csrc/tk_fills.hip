@@ -1,0 +1,611 @@
+// tk_fills.hip -- streaming fill kernels: uniform, bounded, f32 normal, dropout, Philox.
+//
+// One design serves every fill here.  The output is cut into whole 16-byte vectors from
+// its first 16-byte boundary; each lane computes the draws of one vector and writes it
+// with one 16-byte store, so a wave64 store instruction covers 1 KiB of contiguous HBM.
+// A work-group handles U consecutive runs of 256 vectors (4 KiB each), one per unrolled
+// step, so U independent vectors are in flight per lane.  The few elements before the
+// first boundary and after the last whole vector are written one at a time by block 0.
+//
+// Because every 32-bit word of the stream is its own counter, word-sized and wider draws
+// never straddle a vector.  Sub-word draws (u8, u16, f16, bool), Box-Muller pairs at odd
+// starts and Philox blocks at starts that are not a multiple of four straddle by at most
+// one word, pair or block: that piece comes from the next lane through ds_bpermute, and
+// the last lane of a wave computes it itself.  No LDS staging and no extra HBM traffic.
+#include "tk_device.h"
+#include "tk_internal.h"
+
+namespace tk {
+
+// ---------------------------------------------------------------------------------------
+// Geometry and the generic kernel
+// ---------------------------------------------------------------------------------------
+template <class T>
+struct FillBase {
+  static constexpr int E = 16 / (int)sizeof(T);  // elements per 16-byte vector
+  T *out;
+  uint64_t start;  // draw of element 0
+  uint64_t head;   // elements before the first 16-byte boundary
+  uint64_t nvec;   // whole vectors
+  uint32_t tail;   // elements after the last whole vector
+  __device__ __forceinline__ void *vec_ptr(uint64_t v) const { return (void *)(out + head + v * E); }
+  __device__ __forceinline__ uint64_t vec_draw(uint64_t v) const { return start + head + v * E; }
+};
+
+template <class Base, class T>
+static void set_geometry(Base &op, T *out, uint64_t start, uint64_t n) {
+  constexpr uint64_t E = 16 / sizeof(T);
+  uint64_t mis = (uint64_t)((uintptr_t)out & 15u);
+  uint64_t head = mis ? (16 - mis) / sizeof(T) : 0;
+  if (head > n) head = n;
+  op.out = out;
+  op.start = start;
+  op.head = head;
+  op.nvec = (n - head) / E;
+  op.tail = (uint32_t)(n - head - op.nvec * E);
+}
+
+// Writes the head and tail elements (fewer than 16 each) from block 0.
+template <class Op>
+__device__ __forceinline__ void write_edges(const Op &op) {
+  const uint32_t t = threadIdx.x;
+  if (t < op.head) op.out[t] = op.elem(t);
+  if (t >= 128 && t - 128 < op.tail) {
+    uint64_t k = op.head + op.nvec * Op::E + (t - 128);
+    op.out[k] = op.elem(k);
+  }
+}
+
+template <class Op, int U, bool kNT>
+__global__ __launch_bounds__(kBlock) void k_vec_fill(Op op, uint64_t ntiles) {
+  for (uint64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+    const uint64_t v0 = tile * (uint64_t)(kBlock * U) + threadIdx.x;
+    uint4 r[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) r[u] = op.vec(v0 + (uint64_t)u * kBlock);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint64_t v = v0 + (uint64_t)u * kBlock;
+      if (v < op.nvec) store16<kNT>(op.vec_ptr(v), r[u]);
+    }
+  }
+  if (blockIdx.x == 0) write_edges(op);
+}
+
+constexpr int kUnroll = 4;
+
+template <class Op>
+static tk_status launch_vec(const Op &op, hipStream_t stream) {
+  const uint64_t per_tile = (uint64_t)kBlock * kUnroll;
+  uint64_t ntiles = (op.nvec + per_tile - 1) / per_tile;
+  uint64_t grid = ntiles ? ntiles : 1;
+  if (grid > config().max_blocks) grid = config().max_blocks;
+  if (grid > 0x7FFFFFFFull) grid = 0x7FFFFFFFull;
+  if (config().nt_stores)
+    hipLaunchKernelGGL((k_vec_fill<Op, kUnroll, true>), dim3((uint32_t)grid), dim3(kBlock), 0, stream, op, ntiles);
+  else
+    hipLaunchKernelGGL((k_vec_fill<Op, kUnroll, false>), dim3((uint32_t)grid), dim3(kBlock), 0, stream, op, ntiles);
+  return launch_status();
+}
+
+__device__ __forceinline__ uint4 u4(uint32_t a, uint32_t b, uint32_t c, uint32_t d) { return make_uint4(a, b, c, d); }
+__device__ __forceinline__ uint32_t lo32(uint64_t x) { return (uint32_t)x; }
+__device__ __forceinline__ uint32_t hi32(uint64_t x) { return (uint32_t)(x >> 32); }
+
+// ---------------------------------------------------------------------------------------
+// Uniform fills
+// ---------------------------------------------------------------------------------------
+// u32 / f32: draw i is word i.
+template <bool kFloat>
+struct OpWord32 : FillBase<uint32_t> {
+  uint32_t hk;
+  __device__ __forceinline__ uint32_t xf(uint32_t w) const { return kFloat ? __float_as_uint(unit23(w)) : w; }
+  __device__ __forceinline__ uint32_t elem(uint64_t k) const { return xf(word(hk, (uint32_t)(start + k))); }
+  __device__ __forceinline__ uint4 vec(uint64_t v) const {
+    const uint32_t c = (uint32_t)vec_draw(v);
+    return u4(xf(word(hk, c)), xf(word(hk, c + 1)), xf(word(hk, c + 2)), xf(word(hk, c + 3)));
+  }
+};
+
+// u64 / f64: draw i is words 2i (low) and 2i+1 (high).
+template <bool kFloat>
+struct OpWord64 : FillBase<uint64_t> {
+  uint32_t hk;
+  __device__ __forceinline__ uint64_t xf(uint32_t lo, uint32_t hi) const {
+    if (kFloat) return (uint64_t)__double_as_longlong(unit53_lowbits(lo, hi));
+    return (uint64_t)lo | ((uint64_t)hi << 32);
+  }
+  __device__ __forceinline__ uint64_t elem(uint64_t k) const {
+    const uint32_t c = 2u * (uint32_t)(start + k);
+    return xf(word(hk, c), word(hk, c + 1));
+  }
+  __device__ __forceinline__ uint4 vec(uint64_t v) const {
+    const uint32_t c = 2u * (uint32_t)vec_draw(v);
+    uint64_t a = xf(word(hk, c), word(hk, c + 1));
+    uint64_t b = xf(word(hk, c + 2), word(hk, c + 3));
+    return u4(lo32(a), hi32(a), lo32(b), hi32(b));
+  }
+};
+
+// Four consecutive stream words starting `shift` bytes into word w0: lane-local words
+// w0..w0+3, the fifth from the next lane (the last lane of the wave hashes it).
+// `shift` is uniform across the launch.
+__device__ __forceinline__ uint4 words_at_byte(uint32_t hk, uint32_t w0, uint32_t shift) {
+  uint32_t a0 = word(hk, w0), a1 = word(hk, w0 + 1), a2 = word(hk, w0 + 2), a3 = word(hk, w0 + 3);
+  if (shift == 0) return u4(a0, a1, a2, a3);
+  uint32_t a4 = from_next_lane(a0);
+  if (lane_id() == 63) a4 = word(hk, w0 + 4);
+  return u4(__builtin_amdgcn_alignbyte(a1, a0, shift), __builtin_amdgcn_alignbyte(a2, a1, shift),
+            __builtin_amdgcn_alignbyte(a3, a2, shift), __builtin_amdgcn_alignbyte(a4, a3, shift));
+}
+
+// u16 / f16 bits: draw i is half i&1 of word i>>1.
+template <bool kHalf>
+struct OpSub16 : FillBase<uint16_t> {
+  uint32_t hk;
+  __device__ __forceinline__ uint16_t elem(uint64_t k) const {
+    const uint64_t i = start + k;
+    uint32_t h = word(hk, (uint32_t)(i >> 1)) >> (16u * (uint32_t)(i & 1u));
+    return (uint16_t)(kHalf ? half_pair_bits(h) : h);
+  }
+  __device__ __forceinline__ uint4 vec(uint64_t v) const {
+    const uint64_t i0 = vec_draw(v);
+    uint4 w = words_at_byte(hk, (uint32_t)(i0 >> 1), 2u * (uint32_t)(i0 & 1u));
+    if (kHalf) w = u4(half_pair_bits(w.x), half_pair_bits(w.y), half_pair_bits(w.z), half_pair_bits(w.w));
+    return w;
+  }
+};
+
+// u8: draw i is byte i&3 of word i>>2.
+struct OpU8 : FillBase<uint8_t> {
+  uint32_t hk;
+  __device__ __forceinline__ uint8_t elem(uint64_t k) const {
+    const uint64_t i = start + k;
+    return (uint8_t)(word(hk, (uint32_t)(i >> 2)) >> (8u * (uint32_t)(i & 3u)));
+  }
+  __device__ __forceinline__ uint4 vec(uint64_t v) const {
+    const uint64_t i0 = vec_draw(v);
+    return words_at_byte(hk, (uint32_t)(i0 >> 2), (uint32_t)(i0 & 3u));
+  }
+};
+
+// bool: draw i is bit i&31 of word i>>5, one byte 0/1 per bit.
+struct OpBool : FillBase<uint8_t> {
+  uint32_t hk;
+  __device__ __forceinline__ uint8_t elem(uint64_t k) const {
+    const uint64_t i = start + k;
+    return (uint8_t)((word(hk, (uint32_t)(i >> 5)) >> (uint32_t)(i & 31u)) & 1u);
+  }
+  __device__ __forceinline__ uint4 vec(uint64_t v) const {
+    const uint64_t b0 = vec_draw(v);
+    const uint32_t wi = (uint32_t)(b0 >> 5);
+    const uint32_t lo = word(hk, wi), hi = word(hk, wi + 1);
+    const uint32_t bits = __builtin_amdgcn_alignbit(hi, lo, (uint32_t)(b0 & 31u));
+    return u4(nibble_to_bytes(bits, 0), nibble_to_bytes(bits, 4), nibble_to_bytes(bits, 8), nibble_to_bytes(bits, 12));
+  }
+};
+
+// ---------------------------------------------------------------------------------------
+// Bounded integers (Lemire, exact threshold; rejected draws continue on the substream)
+// ---------------------------------------------------------------------------------------
+struct Below32Params {
+  uint32_t hk, hkp, s, t;
+  int64_t low;
+};
+
+// u32 / i32 out, one word per element.
+template <class T>
+struct OpBelow32 : FillBase<T> {
+  Below32Params p;
+  __device__ __forceinline__ T elem(uint64_t k) const {
+    const uint32_t i = (uint32_t)(this->start + k);
+    return (T)((uint32_t)p.low + lemire32(word(p.hk, i), p.s, p.t, p.hkp, i));
+  }
+  __device__ __forceinline__ uint4 vec(uint64_t v) const {
+    const uint32_t i = (uint32_t)this->vec_draw(v);
+    uint32_t r[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) r[j] = (uint32_t)p.low + lemire32(word(p.hk, i + j), p.s, p.t, p.hkp, i + j);
+    return u4(r[0], r[1], r[2], r[3]);
+  }
+};
+
+// i64 out from one word per element: each 16-byte vector holds two elements.
+struct OpBelow32To64 : FillBase<int64_t> {
+  Below32Params p;
+  __device__ __forceinline__ int64_t elem(uint64_t k) const {
+    const uint32_t i = (uint32_t)(start + k);
+    return p.low + (int64_t)lemire32(word(p.hk, i), p.s, p.t, p.hkp, i);
+  }
+  __device__ __forceinline__ uint4 vec(uint64_t v) const {
+    const uint32_t i = (uint32_t)vec_draw(v);
+    uint64_t a = (uint64_t)(p.low + (int64_t)lemire32(word(p.hk, i), p.s, p.t, p.hkp, i));
+    uint64_t b = (uint64_t)(p.low + (int64_t)lemire32(word(p.hk, i + 1), p.s, p.t, p.hkp, i + 1));
+    return u4(lo32(a), hi32(a), lo32(b), hi32(b));
+  }
+};
+
+// u64 / i64 out from one 64-bit draw per element.
+template <class T, bool kSmall>
+struct OpBelow64 : FillBase<T> {
+  uint32_t hk, hkp;
+  uint64_t s, t;
+  int64_t low;
+  __device__ __forceinline__ uint64_t one(uint32_t i) const {
+    const uint32_t c = 2u * i;
+    uint64_t x = (uint64_t)word(hk, c) | ((uint64_t)word(hk, c + 1) << 32);
+    return (uint64_t)low + lemire64<kSmall>(x, s, t, hkp, i);
+  }
+  __device__ __forceinline__ T elem(uint64_t k) const { return (T)one((uint32_t)(this->start + k)); }
+  __device__ __forceinline__ uint4 vec(uint64_t v) const {
+    const uint32_t i = (uint32_t)this->vec_draw(v);
+    uint64_t a = one(i), b = one(i + 1);
+    return u4(lo32(a), hi32(a), lo32(b), hi32(b));
+  }
+};
+
+// ---------------------------------------------------------------------------------------
+// f32 normal: Box-Muller pairs (draw i belongs to pair i >> 1; even i cos, odd i sin)
+// ---------------------------------------------------------------------------------------
+struct OpNormalF32 : FillBase<float> {
+  uint32_t hk;
+  __device__ __forceinline__ void pair(uint32_t c, float *cs, float *sn) const {
+    const float u1 = unit23(word(hk, 2u * c));
+    const float u2 = unit23(word(hk, 2u * c + 1u));
+    const float r = sqrtf(-2.0f * logf(1.0f - u1));
+    const float t = u2 >= 0.5f ? u2 - 1.0f : u2;  // a whole turn: angle in [-pi, pi)
+    float s, co;
+    sincospif(2.0f * t, &s, &co);
+    *cs = r * co;
+    *sn = r * s;
+  }
+  __device__ __forceinline__ float elem(uint64_t k) const {
+    const uint64_t i = start + k;
+    float c, s;
+    pair((uint32_t)(i >> 1), &c, &s);
+    return (i & 1u) ? s : c;
+  }
+  __device__ __forceinline__ uint4 vec(uint64_t v) const {
+    const uint64_t i0 = vec_draw(v);
+    const uint32_t c0 = (uint32_t)(i0 >> 1);
+    float a, b, c, d;
+    pair(c0, &a, &b);
+    pair(c0 + 1, &c, &d);
+    if ((i0 & 1u) == 0) return u4(__float_as_uint(a), __float_as_uint(b), __float_as_uint(c), __float_as_uint(d));
+    // Odd start: the vector is sin(c0), pair c0+1, cos(c0+2); cos(c0+2) is the next
+    // lane's first value.
+    float e = from_next_lane(a);
+    if (lane_id() == 63) {
+      float s_unused;
+      pair(c0 + 2, &e, &s_unused);
+    }
+    return u4(__float_as_uint(b), __float_as_uint(c), __float_as_uint(d), __float_as_uint(e));
+  }
+};
+
+// ---------------------------------------------------------------------------------------
+// Fused dropout: y = u >= p ? x / (1 - p) : +0 (IEEE f32 division), optional mask bytes
+// ---------------------------------------------------------------------------------------
+struct OpDropout : FillBase<float> {
+  const float *x;
+  uint8_t *mask;
+  uint32_t hk;
+  float p, q;
+  bool x_vec;      // x is 16-byte aligned where y is
+  bool mask_word;  // mask is 4-byte aligned where y is 16-byte aligned
+  __device__ __forceinline__ float elem(uint64_t k) const {
+    const bool keep = unit23(word(hk, (uint32_t)(start + k))) >= p;
+    if (mask) mask[k] = (uint8_t)keep;
+    return keep ? __fdiv_rn(x[k], q) : 0.0f;
+  }
+  __device__ __forceinline__ uint4 vec(uint64_t v) const {
+    if (v >= nvec) return u4(0, 0, 0, 0);  // never read x past the end
+    const uint64_t k0 = head + 4 * v;
+    float xv[4];
+    if (x_vec) {
+      float4 t = *(const float4 *)(x + k0);
+      xv[0] = t.x; xv[1] = t.y; xv[2] = t.z; xv[3] = t.w;
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) xv[j] = x[k0 + j];
+    }
+    const uint32_t c = (uint32_t)(start + k0);
+    uint32_t y[4], m = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bool keep = unit23(word(hk, c + j)) >= p;
+      y[j] = keep ? __float_as_uint(__fdiv_rn(xv[j], q)) : 0u;
+      m |= (uint32_t)keep << (8 * j);
+    }
+    if (mask) {
+      if (mask_word) *(uint32_t *)(mask + k0) = m;
+      else
+#pragma unroll
+        for (int j = 0; j < 4; ++j) mask[k0 + j] = (uint8_t)(m >> (8 * j));
+    }
+    return u4(y[0], y[1], y[2], y[3]);
+  }
+};
+
+// ---------------------------------------------------------------------------------------
+// Philox4x32-10 word source
+// ---------------------------------------------------------------------------------------
+// Four consecutive Philox words starting at word w0 (word offset w0 & 3 uniform across the
+// launch): the lane's own block plus, at unaligned offsets, the head of the next lane's.
+__device__ __forceinline__ uint4 philox_words(uint64_t w0, uint32_t k0, uint32_t k1) {
+  const uint64_t b = w0 >> 2;
+  const uint32_t o = (uint32_t)(w0 & 3u);
+  U32x4 B = philox4x32_10(b, k0, k1);
+  if (o == 0) return u4(B.a, B.b, B.c, B.d);
+  uint32_t n0 = from_next_lane(B.a), n1 = from_next_lane(B.b), n2 = from_next_lane(B.c);
+  if (lane_id() == 63) {
+    U32x4 N = philox4x32_10(b + 1, k0, k1);
+    n0 = N.a; n1 = N.b; n2 = N.c;
+  }
+  if (o == 1) return u4(B.b, B.c, B.d, n0);
+  if (o == 2) return u4(B.c, B.d, n0, n1);
+  return u4(B.d, n0, n1, n2);
+}
+
+__device__ __forceinline__ uint32_t philox_word(uint64_t w, uint32_t k0, uint32_t k1) {
+  U32x4 B = philox4x32_10(w >> 2, k0, k1);
+  const uint32_t o = (uint32_t)(w & 3u);
+  return o == 0 ? B.a : o == 1 ? B.b : o == 2 ? B.c : B.d;
+}
+
+template <bool kFloat>
+struct OpPhilox32 : FillBase<uint32_t> {
+  uint32_t k0, k1;
+  __device__ __forceinline__ uint32_t xf(uint32_t w) const { return kFloat ? __float_as_uint(unit23(w)) : w; }
+  __device__ __forceinline__ uint32_t elem(uint64_t k) const { return xf(philox_word(start + k, k0, k1)); }
+  __device__ __forceinline__ uint4 vec(uint64_t v) const {
+    uint4 w = philox_words(vec_draw(v), k0, k1);
+    return u4(xf(w.x), xf(w.y), xf(w.z), xf(w.w));
+  }
+};
+
+template <bool kFloat>
+struct OpPhilox64 : FillBase<uint64_t> {
+  uint32_t k0, k1;
+  __device__ __forceinline__ uint64_t xf(uint32_t lo, uint32_t hi) const {
+    if (kFloat) return (uint64_t)__double_as_longlong(unit53_lowbits(lo, hi));
+    return (uint64_t)lo | ((uint64_t)hi << 32);
+  }
+  __device__ __forceinline__ uint64_t elem(uint64_t k) const {
+    const uint64_t w = 2 * (start + k);
+    return xf(philox_word(w, k0, k1), philox_word(w + 1, k0, k1));
+  }
+  __device__ __forceinline__ uint4 vec(uint64_t v) const {
+    uint4 w = philox_words(2 * vec_draw(v), k0, k1);
+    uint64_t a = xf(w.x, w.y), b = xf(w.z, w.w);
+    return u4(lo32(a), hi32(a), lo32(b), hi32(b));
+  }
+};
+
+}  // namespace tk
+
+// =======================================================================================
+// C ABI entry points
+// =======================================================================================
+using namespace tk;
+
+namespace {
+
+// Draws needed by a fill of n elements from `start` must all be <= dmax.
+tk_status check_draws(uint64_t start, uint64_t n, uint64_t dmax) {
+  if (start > dmax || n - 1 > dmax - start) return TK_ERANGE;
+  return TK_OK;
+}
+
+template <class T>
+bool elem_aligned(const T *p) { return ((uintptr_t)p % sizeof(T)) == 0; }
+
+constexpr uint64_t kMaxW32 = 0xFFFFFFFFull;        // one word per draw
+constexpr uint64_t kMaxW64 = 0x7FFFFFFFull;        // two words per draw
+constexpr uint64_t kMaxU16 = 0x1FFFFFFFFull;       // half a word per draw
+constexpr uint64_t kMaxU8 = 0x3FFFFFFFFull;        // a quarter word per draw
+constexpr uint64_t kMaxBool = 0x1FFFFFFFFFull;     // a bit per draw
+constexpr uint64_t kMaxPhilox64 = 0x7FFFFFFFFFFFFFFFull;
+
+#define TK_PRECHECK(ptr, dmax)                         \
+  do {                                                 \
+    if (n == 0) return TK_OK;                          \
+    if (!(ptr) || !elem_aligned(ptr)) return TK_EINVAL; \
+    tk_status st_ = check_draws(start_draw, n, (dmax)); \
+    if (st_ != TK_OK) return st_;                      \
+  } while (0)
+
+template <class Op, class T>
+tk_status run_simple(Op op, T *out, uint64_t start, uint64_t n, hipStream_t stream) {
+  set_geometry(op, out, start, n);
+  return launch_vec(op, stream);
+}
+
+static Below32Params below32_params(uint32_t key, uint32_t bound, int64_t low) {
+  Below32Params p;
+  p.hk = host_lowbias32(key);
+  p.hkp = host_substream_key(key, kPurposeBelow32);
+  p.s = bound;
+  p.t = (uint32_t)(0u - bound) % bound;
+  p.low = low;
+  return p;
+}
+
+template <class T>
+static tk_status below64(uint32_t key, uint64_t start_draw, uint64_t n, int64_t low, uint64_t bound, T *out,
+                         hipStream_t stream) {
+  const uint32_t hk = host_lowbias32(key), hkp = host_substream_key(key, kPurposeBelow64);
+  const uint64_t t = (0ull - bound) % bound;
+  if (bound <= 0xFFFFFFFFull) {
+    OpBelow64<T, true> op{};
+    op.hk = hk; op.hkp = hkp; op.s = bound; op.t = t; op.low = low;
+    return run_simple(op, out, start_draw, n, stream);
+  }
+  OpBelow64<T, false> op{};
+  op.hk = hk; op.hkp = hkp; op.s = bound; op.t = t; op.low = low;
+  return run_simple(op, out, start_draw, n, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+tk_status tk_fill_u32(uint32_t key, uint64_t start_draw, uint64_t n, uint32_t *out, hipStream_t stream) {
+  TK_PRECHECK(out, kMaxW32);
+  OpWord32<false> op{};
+  op.hk = host_lowbias32(key);
+  return run_simple(op, out, start_draw, n, stream);
+}
+
+tk_status tk_fill_f32(uint32_t key, uint64_t start_draw, uint64_t n, float *out, hipStream_t stream) {
+  TK_PRECHECK(out, kMaxW32);
+  OpWord32<true> op{};
+  op.hk = host_lowbias32(key);
+  return run_simple(op, (uint32_t *)out, start_draw, n, stream);
+}
+
+tk_status tk_fill_u64(uint32_t key, uint64_t start_draw, uint64_t n, uint64_t *out, hipStream_t stream) {
+  TK_PRECHECK(out, kMaxW64);
+  OpWord64<false> op{};
+  op.hk = host_lowbias32(key);
+  return run_simple(op, out, start_draw, n, stream);
+}
+
+tk_status tk_fill_f64(uint32_t key, uint64_t start_draw, uint64_t n, double *out, hipStream_t stream) {
+  TK_PRECHECK(out, kMaxW64);
+  OpWord64<true> op{};
+  op.hk = host_lowbias32(key);
+  return run_simple(op, (uint64_t *)out, start_draw, n, stream);
+}
+
+tk_status tk_fill_u16(uint32_t key, uint64_t start_draw, uint64_t n, uint16_t *out, hipStream_t stream) {
+  TK_PRECHECK(out, kMaxU16);
+  OpSub16<false> op{};
+  op.hk = host_lowbias32(key);
+  return run_simple(op, out, start_draw, n, stream);
+}
+
+tk_status tk_fill_f16_bits(uint32_t key, uint64_t start_draw, uint64_t n, uint16_t *out, hipStream_t stream) {
+  TK_PRECHECK(out, kMaxU16);
+  OpSub16<true> op{};
+  op.hk = host_lowbias32(key);
+  return run_simple(op, out, start_draw, n, stream);
+}
+
+tk_status tk_fill_u8(uint32_t key, uint64_t start_draw, uint64_t n, uint8_t *out, hipStream_t stream) {
+  TK_PRECHECK(out, kMaxU8);
+  OpU8 op{};
+  op.hk = host_lowbias32(key);
+  return run_simple(op, out, start_draw, n, stream);
+}
+
+tk_status tk_fill_bool(uint32_t key, uint64_t start_draw, uint64_t n, uint8_t *out, hipStream_t stream) {
+  TK_PRECHECK(out, kMaxBool);
+  OpBool op{};
+  op.hk = host_lowbias32(key);
+  return run_simple(op, out, start_draw, n, stream);
+}
+
+tk_status tk_fill_u32_below(uint32_t key, uint64_t start_draw, uint64_t n, uint32_t bound, uint32_t *out,
+                            hipStream_t stream) {
+  if (bound == 0) return TK_EINVAL;
+  TK_PRECHECK(out, kMaxW32);
+  OpBelow32<uint32_t> op{};
+  op.p = below32_params(key, bound, 0);
+  return run_simple(op, out, start_draw, n, stream);
+}
+
+tk_status tk_fill_i32_below(uint32_t key, uint64_t start_draw, uint64_t n, int32_t low, uint32_t bound,
+                            int32_t *out, hipStream_t stream) {
+  if (bound == 0) return TK_EINVAL;
+  if ((int64_t)low + (int64_t)bound - 1 > (int64_t)INT32_MAX) return TK_ERANGE;
+  TK_PRECHECK(out, kMaxW32);
+  OpBelow32<int32_t> op{};
+  op.p = below32_params(key, bound, low);
+  return run_simple(op, out, start_draw, n, stream);
+}
+
+tk_status tk_fill_i64_below32(uint32_t key, uint64_t start_draw, uint64_t n, int64_t low, uint32_t bound,
+                              int64_t *out, hipStream_t stream) {
+  if (bound == 0) return TK_EINVAL;
+  if ((__int128)low + (__int128)bound - 1 > (__int128)INT64_MAX) return TK_ERANGE;
+  TK_PRECHECK(out, kMaxW32);
+  OpBelow32To64 op{};
+  op.p = below32_params(key, bound, low);
+  return run_simple(op, out, start_draw, n, stream);
+}
+
+tk_status tk_fill_u64_below(uint32_t key, uint64_t start_draw, uint64_t n, uint64_t bound, uint64_t *out,
+                            hipStream_t stream) {
+  if (bound == 0) return TK_EINVAL;
+  TK_PRECHECK(out, kMaxW64);
+  return below64<uint64_t>(key, start_draw, n, 0, bound, out, stream);
+}
+
+tk_status tk_fill_i64_below(uint32_t key, uint64_t start_draw, uint64_t n, int64_t low, uint64_t bound,
+                            int64_t *out, hipStream_t stream) {
+  if (bound == 0) return TK_EINVAL;
+  if ((__int128)low + (__int128)bound - 1 > (__int128)INT64_MAX) return TK_ERANGE;
+  TK_PRECHECK(out, kMaxW64);
+  return below64<int64_t>(key, start_draw, n, low, bound, out, stream);
+}
+
+tk_status tk_fill_normal_f32(uint32_t key, uint64_t start_draw, uint64_t n, float *out, hipStream_t stream) {
+  TK_PRECHECK(out, kMaxW32);
+  OpNormalF32 op{};
+  op.hk = host_lowbias32(key);
+  return run_simple(op, out, start_draw, n, stream);
+}
+
+tk_status tk_dropout_f32(uint32_t key, uint64_t start_draw, uint64_t n, float p, const float *x, float *y,
+                         uint8_t *mask, hipStream_t stream) {
+  if (!(p >= 0.0f && p < 1.0f)) return TK_EINVAL;
+  if (n == 0) return TK_OK;
+  if (!x || !y || !elem_aligned(x) || !elem_aligned(y)) return TK_EINVAL;
+  if (x != y) {  // in place is allowed; any other overlap is not
+    const uintptr_t xa = (uintptr_t)x, ya = (uintptr_t)y, bytes = (uintptr_t)(n * sizeof(float));
+    if (xa < ya + bytes && ya < xa + bytes) return TK_EINVAL;
+  }
+  tk_status st = check_draws(start_draw, n, kMaxW32);
+  if (st != TK_OK) return st;
+  OpDropout op{};
+  set_geometry(op, y, start_draw, n);
+  op.x = x;
+  op.mask = mask;
+  op.hk = host_lowbias32(key);
+  op.p = p;
+  op.q = 1.0f - p;
+  op.x_vec = (((uintptr_t)(x + op.head)) & 15u) == 0;
+  op.mask_word = mask && (((uintptr_t)(mask + op.head)) & 3u) == 0;
+  return launch_vec(op, stream);
+}
+
+tk_status tk_philox_fill_u32(uint64_t key, uint64_t start_draw, uint64_t n, uint32_t *out, hipStream_t stream) {
+  TK_PRECHECK(out, ~0ull);
+  OpPhilox32<false> op{};
+  op.k0 = (uint32_t)key; op.k1 = (uint32_t)(key >> 32);
+  return run_simple(op, out, start_draw, n, stream);
+}
+
+tk_status tk_philox_fill_f32(uint64_t key, uint64_t start_draw, uint64_t n, float *out, hipStream_t stream) {
+  TK_PRECHECK(out, ~0ull);
+  OpPhilox32<true> op{};
+  op.k0 = (uint32_t)key; op.k1 = (uint32_t)(key >> 32);
+  return run_simple(op, (uint32_t *)out, start_draw, n, stream);
+}
+
+tk_status tk_philox_fill_u64(uint64_t key, uint64_t start_draw, uint64_t n, uint64_t *out, hipStream_t stream) {
+  TK_PRECHECK(out, kMaxPhilox64);
+  OpPhilox64<false> op{};
+  op.k0 = (uint32_t)key; op.k1 = (uint32_t)(key >> 32);
+  return run_simple(op, out, start_draw, n, stream);
+}
+
+tk_status tk_philox_fill_f64(uint64_t key, uint64_t start_draw, uint64_t n, double *out, hipStream_t stream) {
+  TK_PRECHECK(out, kMaxPhilox64);
+  OpPhilox64<true> op{};
+  op.k0 = (uint32_t)key; op.k1 = (uint32_t)(key >> 32);
+  return run_simple(op, (uint64_t *)out, start_draw, n, stream);
+}
+
+}  // extern "C"

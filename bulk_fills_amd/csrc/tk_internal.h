@@ -1,0 +1,65 @@
+// tk_internal.h -- host-side helpers shared by the libtk translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <mutex>
+
+#include "tk.h"
+
+namespace tk {
+
+// Last HIP error seen by this thread (reported by tk_last_hip_error).
+void set_hip_error(hipError_t e);
+
+// Maps a HIP error to TK_EHIP (recording it) or TK_OK.
+inline tk_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return TK_OK;
+  set_hip_error(e);
+  return TK_EHIP;
+}
+
+// Status of the most recent kernel launch on this thread.
+inline tk_status launch_status() { return hip_status(hipGetLastError()); }
+
+// Host copy of the generator (the kernels use the __device__ one in tk_device.h).
+inline uint32_t host_lowbias32(uint32_t x) {
+  x ^= x >> 16;
+  x *= 0x7FEB352Du;
+  x ^= x >> 15;
+  x *= 0x846CA68Bu;
+  x ^= x >> 16;
+  return x;
+}
+
+// Purpose tags of sub(key, P) (ASCII "NORM", "BL32", "BL64").
+constexpr uint32_t kPurposeNormal64 = 0x4E4F524Du;
+constexpr uint32_t kPurposeBelow32 = 0x424C3332u;
+constexpr uint32_t kPurposeBelow64 = 0x424C3634u;
+
+// lowbias32(sub(key, P)) with sub(key, P) = lowbias32(lowbias32(key) ^ P): the value the
+// kernels need to open the substream of any draw for purpose P.
+inline uint32_t host_substream_key(uint32_t key, uint32_t purpose) {
+  return host_lowbias32(host_lowbias32(host_lowbias32(key) ^ purpose));
+}
+
+// Tunables read once from the environment (benchmarks and tests only; defaults are the
+// measured best).
+struct Config {
+  bool nt_stores;           // TK_STORE=nt: non-temporal 16-byte stores
+  uint64_t max_blocks;      // TK_MAX_BLOCKS: cap on the grid of the streaming fills
+  int zig_blocks_per_cu;    // TK_ZIG_BLOCKS_PER_CU: persistent grid of the ziggurat pass
+  int choice_blocks_per_cu; // TK_CHOICE_BLOCKS_PER_CU: persistent grid of the choice fill
+};
+const Config &config();
+
+// Compute units of the current device (cached per device).
+int device_cus(int device);
+
+// Current device, or a negative value with the error recorded.
+int current_device(tk_status *st);
+
+constexpr int kMaxDevices = 64;
+
+}  // namespace tk

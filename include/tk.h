@@ -1,0 +1,163 @@
+/*
+ * tk.h -- C ABI of libtk: counter-based random bulk fills into the device memory of one
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Contract (tandem-sycl, "Design", §Fills and §Normals): element k of a fill takes draw
+ * i = start_draw + k, and its value is a pure function of (key, i).  A fill cut at any
+ * element therefore equals the whole fill, and resuming a fill is a call with a larger
+ * start_draw.  A start draw is an offset into the stream (tandem-cuda, "Performance",
+ * §GPU: a row's start draw is a generator offset).
+ *
+ * Generator (Phobos stdlib, "Random numbers", §hash32 and §uniform): the lowbias32 hash,
+ * word(key, c) = hash32(c ^ hash32(key)) for 32-bit key and counter.  Word c is the
+ * stream's c-th 32-bit word; narrower draws are its little-endian parts and 64-bit draws
+ * are the word pair (2i, 2i+1), low word first.  A fill whose counters would reach 2^32
+ * is refused with TK_ERANGE instead of wrapping.
+ *
+ * Conventions for every call:
+ *   - Pointers `out`, `x`, `y`, `mask` are device pointers owned by the caller; they must
+ *     stay valid until the work enqueued on `stream` has finished.  The library never
+ *     keeps them.  `out` must be aligned to its element size; any such alignment is
+ *     accepted (16-byte stores are used where the address allows).
+ *   - Calls are asynchronous and ordered on `stream` (NULL = the device's null stream)
+ *     on the device current to the calling host thread.  Any host thread may call.
+ *   - Arguments are checked before anything is enqueued; on any error nothing is
+ *     enqueued.  n == 0 is TK_OK and enqueues nothing.  There is no CPU fallback.
+ *   - TK_EHIP reports a HIP runtime failure; tk_last_hip_error() gives its code for the
+ *     calling thread.
+ */
+#ifndef TK_H
+#define TK_H
+
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum tk_status {
+    TK_OK = 0,
+    TK_EINVAL = 1, /* bad argument: NULL pointer, misaligned pointer, bad bound or p */
+    TK_ERANGE = 2, /* draws beyond the 2^32-word counter space, or a bounded range whose
+                      top does not fit the output type */
+    TK_ENOMEM = 3, /* the library could not allocate its own device state */
+    TK_EHIP = 4    /* a HIP runtime call failed */
+} tk_status;
+
+/* ---- Uniform fills ------------------------------------------------------------------
+ * tandem-cuda, "Performance", §GPU table (fill_u8 ... fill_bool rows); narrow types write
+ * fewer bytes of the same stream.
+ *   u8:  draw i is byte i&3 of word i>>2          (i < 2^34)
+ *   u16: draw i is half i&1 of word i>>1          (i < 2^33)
+ *   u32: draw i is word i                         (i < 2^32)
+ *   u64: draw i is word 2i | word 2i+1 << 32      (i < 2^31)
+ *   f16_bits: binary16 encoding of (u16 draw & 0x7FF) * 2^-11, a uniform on [0, 1)
+ *   f32: (word i & 0x7FFFFF) * 2^-23 (Phobos, §uniform), exactly
+ *   f64: (u64 draw & (2^53 - 1)) * 2^-53, exactly
+ *   bool: bit i&31 of word i>>5 as one byte 0 or 1 (tandem-sycl, "Design", §Fills: one
+ *         byte per bit)                           (i < 2^37)                              */
+tk_status tk_fill_u8(uint32_t key, uint64_t start_draw, uint64_t n, uint8_t *out, hipStream_t stream);
+tk_status tk_fill_u16(uint32_t key, uint64_t start_draw, uint64_t n, uint16_t *out, hipStream_t stream);
+tk_status tk_fill_u32(uint32_t key, uint64_t start_draw, uint64_t n, uint32_t *out, hipStream_t stream);
+tk_status tk_fill_u64(uint32_t key, uint64_t start_draw, uint64_t n, uint64_t *out, hipStream_t stream);
+tk_status tk_fill_f16_bits(uint32_t key, uint64_t start_draw, uint64_t n, uint16_t *out, hipStream_t stream);
+tk_status tk_fill_f32(uint32_t key, uint64_t start_draw, uint64_t n, float *out, hipStream_t stream);
+tk_status tk_fill_f64(uint32_t key, uint64_t start_draw, uint64_t n, double *out, hipStream_t stream);
+tk_status tk_fill_bool(uint32_t key, uint64_t start_draw, uint64_t n, uint8_t *out, hipStream_t stream);
+
+/* ---- Bounded integers ---------------------------------------------------------------
+ * tandem-cuda, "Performance", §GPU (fill_u32_below, fill_u64_below, "with a low bound"
+ * into int32_t / int64_t); perturbation-kernel, "Backends", §Why the GPU can be exact
+ * (Lemire's multiply-shift with rejection).  Value = high half of x * bound for the
+ * draw x, rejected while the low half is below (2^W - bound) mod bound; a rejected draw
+ * continues on the per-index substream split(i) of sub(key, "BL32"/"BL64").
+ * bound == 0 -> TK_EINVAL.  With `low`, values are low + [0, bound); a top
+ * low + bound - 1 beyond the output type -> TK_ERANGE.
+ *   u32_below, i32_below, i64_below32: one word per element (i < 2^32)
+ *   u64_below, i64_below: one 64-bit draw per element (i < 2^31)                         */
+tk_status tk_fill_u32_below(uint32_t key, uint64_t start_draw, uint64_t n, uint32_t bound,
+                            uint32_t *out, hipStream_t stream);
+tk_status tk_fill_u64_below(uint32_t key, uint64_t start_draw, uint64_t n, uint64_t bound,
+                            uint64_t *out, hipStream_t stream);
+tk_status tk_fill_i32_below(uint32_t key, uint64_t start_draw, uint64_t n, int32_t low,
+                            uint32_t bound, int32_t *out, hipStream_t stream);
+tk_status tk_fill_i64_below32(uint32_t key, uint64_t start_draw, uint64_t n, int64_t low,
+                              uint32_t bound, int64_t *out, hipStream_t stream);
+tk_status tk_fill_i64_below(uint32_t key, uint64_t start_draw, uint64_t n, int64_t low,
+                            uint64_t bound, int64_t *out, hipStream_t stream);
+
+/* ---- Normals ------------------------------------------------------------------------
+ * f64 (tandem-sycl, "Design", §Normals): the 1024-layer equal-area ziggurat, one 64-bit
+ * draw d per element: layer d & 1023, sign bit 10, u = (d >> 11) 2^-53; x = u X[layer] is
+ * taken when below X[layer+1]; the ~0.43 % of draws that miss continue on the
+ * per-index substream split(i) of sub(key, "NORM") (wedge test against exp(-x^2/2), or
+ * the tail beyond r).  Two kernels: a table pass and a continuation pass over the listed
+ * misses; the list and the 16 KiB layer table are per-device library state, ordered
+ * across streams by an event.  i < 2^31.
+ * f32 (tandem-sycl, "Design", §Normals; Phobos, §randn): Box-Muller pairs; draw i
+ * belongs to pair c = i >> 1 built from the f32 uniforms at words 2c and 2c+1:
+ * r = sqrt(-2 ln(1 - u1)), angle 2 pi t with t = u2 wrapped into [-1/2, 1/2); even i
+ * takes r cos, odd i r sin.  i < 2^32.                                                   */
+tk_status tk_fill_normal_f64(uint32_t key, uint64_t start_draw, uint64_t n, double *out, hipStream_t stream);
+tk_status tk_fill_normal_f32(uint32_t key, uint64_t start_draw, uint64_t n, float *out, hipStream_t stream);
+
+/* ---- Fused dropout ------------------------------------------------------------------
+ * Phobos, §dropout: y[k] = uniform(key, start_draw + k) >= p ? x[k] / (1 - p) : +0.0, with
+ * 1 - p and the quotient rounded as f32 operations (a true division).  p must lie in
+ * [0, 1), else TK_EINVAL.  x and y are n floats; they may be the same buffer (in place)
+ * but must not otherwise overlap.  mask (nullable) receives one byte per element, 1 for
+ * kept.  i < 2^32.                                                                       */
+tk_status tk_dropout_f32(uint32_t key, uint64_t start_draw, uint64_t n, float p, const float *x,
+                         float *y, uint8_t *mask, hipStream_t stream);
+
+/* ---- Weighted choice through an alias table -----------------------------------------
+ * tandem-sycl, "Design", §Fills: the choice fill maps each 64-bit draw through an alias
+ * table.  tk_alias_create builds the table on the host from n >= 1 finite, non-negative
+ * host weights with a positive sum (integer Vose construction: index j owns an integer
+ * share of n * 2^32, the rounding remainder going to the largest weight) and uploads it
+ * to the current device; it is synchronous and owns its device memory until
+ * tk_alias_destroy.  The fill maps draw d to column c = (hi32(d) * n) >> 32 and coin
+ * lo32(d): out = coin < q[c] ? c : alias[c].  The table must outlive the stream work that
+ * reads it and be used on the device it was created on.  i < 2^31.                       */
+typedef struct tk_alias tk_alias;
+tk_status tk_alias_create(const double *weights, uint32_t n, tk_alias **table);
+tk_status tk_alias_destroy(tk_alias *table);
+uint32_t tk_alias_size(const tk_alias *table);
+/* The host construction tk_alias_create uploads, alone: writes n entries of q and alias
+ * to host arrays.  Touches no device. */
+tk_status tk_alias_build_host(const double *weights, uint32_t n, uint32_t *q, uint32_t *alias);
+/* Copies the table to host arrays of tk_alias_size() entries each. */
+tk_status tk_alias_export(const tk_alias *table, uint32_t *q, uint32_t *alias);
+tk_status tk_fill_choice_u32(uint32_t key, uint64_t start_draw, uint64_t n, const tk_alias *table,
+                             uint32_t *out, hipStream_t stream);
+
+/* ---- Philox4x32-10 word source ------------------------------------------------------
+ * The counter-based generator of the cuRAND comparison column (tandem-cuda,
+ * "Performance", §GPU); Salmon et al., SC'11.  64-bit key (lo, hi); word w is lane w & 3
+ * of the block with counter (lo32(w >> 2), hi32(w >> 2), 0, 0).  Same draw layout and
+ * float transforms as the lowbias32 fills; the counter space is 64-bit.                  */
+tk_status tk_philox_fill_u32(uint64_t key, uint64_t start_draw, uint64_t n, uint32_t *out, hipStream_t stream);
+tk_status tk_philox_fill_u64(uint64_t key, uint64_t start_draw, uint64_t n, uint64_t *out, hipStream_t stream);
+tk_status tk_philox_fill_f32(uint64_t key, uint64_t start_draw, uint64_t n, float *out, hipStream_t stream);
+tk_status tk_philox_fill_f64(uint64_t key, uint64_t start_draw, uint64_t n, double *out, hipStream_t stream);
+
+/* ---- Status and introspection -------------------------------------------------------*/
+const char *tk_status_string(tk_status status);
+/* The hipError_t of the last TK_EHIP returned to the calling thread (0 if none). */
+int tk_last_hip_error(void);
+/* Copies the 1024-layer table the kernels use: x and f of 1025 doubles each (host). */
+tk_status tk_ziggurat_table(double *x, double *f);
+/* Test hook: caps the f64 normal miss list at `capacity` entries on every device (0
+ * restores automatic sizing), so the continuation pass's whole-fill walk can be forced.
+ * Takes effect at the next tk_fill_normal_f64 call. */
+tk_status tk_debug_set_miss_capacity(uint64_t capacity);
+/* Test hook: waits for the current device's last tk_fill_normal_f64 and returns how many
+ * of its draws missed the fast path (synchronous). */
+tk_status tk_debug_last_miss_count(uint64_t *count);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,132 @@
+"""The C ABI on the CPU: the library loads, exports every symbol include/tk.h declares,
+and refuses bad arguments before any HIP call (so no device is needed here).  Also checks
+the library's host-side tables against the oracle's independent builds, bit for bit."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+import bulk_fills_amd as tk
+import oracle
+import tk_inputs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "tk.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tk_\w+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert len(names) >= 30
+    raw = C.CDLL(tk.LIB_PATH)
+    missing = [n for n in names if not hasattr(raw, n)]
+    assert not missing, missing
+    assert set(tk.SIGNATURES) | {"tk_status_string", "tk_last_hip_error", "tk_alias_size"} >= set(names)
+
+
+def test_binding_names_match_the_c_abi():
+    for name in declared_functions():
+        if name in ("tk_status_string", "tk_last_hip_error", "tk_alias_size", "tk_alias_destroy", "tk_alias_export"):
+            continue
+        assert hasattr(tk, name), name
+
+
+L = tk.lib
+FAKE = 0x10000  # never dereferenced: every call below is refused before any launch
+U32MAX = (1 << 32) - 1
+
+SIMPLE = [("tk_fill_u8", 1, 1 << 34), ("tk_fill_u16", 2, 1 << 33), ("tk_fill_u32", 4, 1 << 32),
+          ("tk_fill_u64", 8, 1 << 31), ("tk_fill_f16_bits", 2, 1 << 33), ("tk_fill_f32", 4, 1 << 32),
+          ("tk_fill_f64", 8, 1 << 31), ("tk_fill_bool", 1, 1 << 37), ("tk_fill_normal_f64", 8, 1 << 31),
+          ("tk_fill_normal_f32", 4, 1 << 32)]
+
+
+@pytest.mark.parametrize("name,size,limit", SIMPLE)
+def test_simple_fill_validation(name, size, limit):
+    f = getattr(L, name)
+    assert f(1, 0, 0, None, None) == tk.TK_OK          # n == 0: nothing to do
+    assert f(1, 0, 0, FAKE + 1, None) == tk.TK_OK      # not even the pointer is looked at
+    assert f(1, 0, 5, None, None) == tk.TK_EINVAL      # NULL output
+    if size > 1:
+        assert f(1, 0, 5, FAKE + 1, None) == tk.TK_EINVAL  # not element aligned
+    assert f(1, limit - 1, 2, FAKE, None) == tk.TK_ERANGE   # crosses the counter space
+    assert f(1, limit, 1, FAKE, None) == tk.TK_ERANGE
+    assert f(1, 1 << 63, 1 << 63, FAKE, None) == tk.TK_ERANGE  # start + n overflows
+
+
+def test_bounded_validation():
+    assert L.tk_fill_u32_below(1, 0, 4, 0, FAKE, None) == tk.TK_EINVAL
+    assert L.tk_fill_u64_below(1, 0, 4, 0, FAKE, None) == tk.TK_EINVAL
+    assert L.tk_fill_u32_below(1, U32MAX, 2, 7, FAKE, None) == tk.TK_ERANGE
+    assert L.tk_fill_u64_below(1, 1 << 31, 1, 7, FAKE, None) == tk.TK_ERANGE
+    assert L.tk_fill_i32_below(1, 0, 4, (1 << 31) - 10, 11, FAKE, None) == tk.TK_ERANGE
+    assert L.tk_fill_i32_below(1, 0, 4, 0, 0, FAKE, None) == tk.TK_EINVAL
+    assert L.tk_fill_i64_below32(1, 0, 4, (1 << 63) - 10, 11, FAKE, None) == tk.TK_ERANGE
+    assert L.tk_fill_i64_below(1, 0, 4, (1 << 63) - 10, 11, FAKE, None) == tk.TK_ERANGE
+    assert L.tk_fill_i64_below(1, 0, 4, 0, 0, FAKE, None) == tk.TK_EINVAL
+    assert L.tk_fill_i32_below(1, 0, 0, 0, 0, None, None) == tk.TK_EINVAL  # bound is checked first
+
+
+def test_dropout_validation():
+    for p in (1.0, -0.25, float("nan"), float("inf")):
+        assert L.tk_dropout_f32(1, 0, 4, p, FAKE, FAKE + 64, None, None) == tk.TK_EINVAL
+    assert L.tk_dropout_f32(1, 0, 4, 0.1, None, FAKE, None, None) == tk.TK_EINVAL
+    assert L.tk_dropout_f32(1, 0, 4, 0.1, FAKE, FAKE + 2, None, None) == tk.TK_EINVAL   # misaligned y
+    assert L.tk_dropout_f32(1, 0, 8, 0.1, FAKE, FAKE + 4, None, None) == tk.TK_EINVAL   # partial overlap
+    assert L.tk_dropout_f32(1, U32MAX, 2, 0.1, FAKE, FAKE + 64, None, None) == tk.TK_ERANGE
+    assert L.tk_dropout_f32(1, 0, 0, 0.1, None, None, None, None) == tk.TK_OK
+
+
+def test_choice_and_alias_validation():
+    w = np.ones(4)
+    h = C.c_void_p()
+    assert L.tk_alias_create(None, 4, C.byref(h)) == tk.TK_EINVAL
+    assert L.tk_alias_create(w.ctypes.data, 0, C.byref(h)) == tk.TK_EINVAL
+    for bad in ([1.0, -1.0], [0.0, 0.0], [1.0, float("nan")], [1.0, float("inf")]):
+        b = np.array(bad)
+        assert L.tk_alias_create(b.ctypes.data, b.size, C.byref(h)) == tk.TK_EINVAL
+    assert L.tk_fill_choice_u32(1, 0, 4, None, FAKE, None) == tk.TK_EINVAL
+    assert L.tk_alias_destroy(None) == tk.TK_EINVAL
+    assert L.tk_alias_size(None) == 0
+
+
+def test_philox_validation():
+    assert L.tk_philox_fill_u32(1, 0, 4, None, None) == tk.TK_EINVAL
+    assert L.tk_philox_fill_u32(1, (1 << 64) - 1, 2, FAKE, None) == tk.TK_ERANGE
+    assert L.tk_philox_fill_u64(1, 1 << 63, 1, FAKE, None) == tk.TK_ERANGE
+    assert L.tk_philox_fill_f64(1, 0, 4, FAKE + 4, None) == tk.TK_EINVAL
+
+
+def test_status_strings():
+    for code in range(5):
+        s = L.tk_status_string(code).decode()
+        assert s.startswith(["TK_OK", "TK_EINVAL", "TK_ERANGE", "TK_ENOMEM", "TK_EHIP"][code])
+    assert L.tk_last_hip_error() == 0
+    assert L.tk_debug_set_miss_capacity(1 << 40) == tk.TK_EINVAL
+    assert L.tk_debug_set_miss_capacity(0) == tk.TK_OK
+
+
+def test_ziggurat_table_is_the_oracles():
+    """Two independent builds (mpmath secant in the package, binary128 bisection in the
+    oracle) of the 1024-layer table agree in every double."""
+    x, f = tk.tk_ziggurat_table()
+    xo, fo, r, v = oracle.zig_table(1024)
+    assert np.array_equal(x.view(np.uint64), xo.view(np.uint64))
+    assert np.array_equal(f.view(np.uint64), fo.view(np.uint64))
+    assert x[1] == r
+
+
+@pytest.mark.parametrize("weights", [
+    [1.0], [1.0, 2.0, 3.0], [0.0, 5.0, 0.0, 1.0], [1.0] * 7, [3.0, 3.0, 1.0],
+    list(tk_inputs.zipf_weights()), list(np.random.default_rng(4).random(5000)),
+])
+def test_alias_host_build_is_the_oracles(weights):
+    q, a = tk.tk_alias_build_host(weights)
+    qo, ao, _ = oracle.alias_build(weights)
+    assert np.array_equal(q, qo) and np.array_equal(a, ao)
