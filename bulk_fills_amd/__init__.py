@@ -65,7 +65,7 @@ SIGNATURES = {
     "tk_philox_fill_f32": [_u64, _u64, _u64, _p, _p],
     "tk_philox_fill_f64": [_u64, _u64, _u64, _p, _p],
     "tk_ziggurat_table": [_p, _p],
-    "tk_debug_set_miss_capacity": [_u64],
+    "tk_debug_set_miss_capacity": [_u32, _u64],
     "tk_debug_last_miss_count": [_p],
 }
 for _name, _args in SIGNATURES.items():
@@ -234,8 +234,8 @@ def tk_ziggurat_table():
     return x, f
 
 
-def tk_debug_set_miss_capacity(capacity):
-    _check(lib.tk_debug_set_miss_capacity(capacity), "tk_debug_set_miss_capacity")
+def tk_debug_set_miss_capacity(per_group, overflow):
+    _check(lib.tk_debug_set_miss_capacity(per_group, overflow), "tk_debug_set_miss_capacity")
 
 
 def tk_debug_last_miss_count():

@@ -72,19 +72,29 @@ __global__ __launch_bounds__(kBlock) void k_vec_fill(Op op, uint64_t ntiles) {
   if (blockIdx.x == 0) write_edges(op);
 }
 
-constexpr int kUnroll = 4;
-
-template <class Op>
-static tk_status launch_vec(const Op &op, hipStream_t stream) {
-  const uint64_t per_tile = (uint64_t)kBlock * kUnroll;
+template <class Op, int U>
+static void launch_vec_u(const Op &op, hipStream_t stream) {
+  const uint64_t per_tile = (uint64_t)kBlock * U;
   uint64_t ntiles = (op.nvec + per_tile - 1) / per_tile;
   uint64_t grid = ntiles ? ntiles : 1;
   if (grid > config().max_blocks) grid = config().max_blocks;
   if (grid > 0x7FFFFFFFull) grid = 0x7FFFFFFFull;
   if (config().nt_stores)
-    hipLaunchKernelGGL((k_vec_fill<Op, kUnroll, true>), dim3((uint32_t)grid), dim3(kBlock), 0, stream, op, ntiles);
+    hipLaunchKernelGGL((k_vec_fill<Op, U, true>), dim3((uint32_t)grid), dim3(kBlock), 0, stream, op, ntiles);
   else
-    hipLaunchKernelGGL((k_vec_fill<Op, kUnroll, false>), dim3((uint32_t)grid), dim3(kBlock), 0, stream, op, ntiles);
+    hipLaunchKernelGGL((k_vec_fill<Op, U, false>), dim3((uint32_t)grid), dim3(kBlock), 0, stream, op, ntiles);
+}
+
+// One vector per lane and one 4 KiB tile per work-group over a grid as large as the
+// output measured fastest for streaming stores on MI355X (more vectors per lane or a
+// persistent grid lowered the store rate); TK_UNROLL=2|4 selects the alternatives.
+template <class Op>
+static tk_status launch_vec(const Op &op, hipStream_t stream) {
+  switch (config().unroll) {
+    case 2: launch_vec_u<Op, 2>(op, stream); break;
+    case 4: launch_vec_u<Op, 4>(op, stream); break;
+    default: launch_vec_u<Op, 1>(op, stream); break;
+  }
   return launch_status();
 }
 

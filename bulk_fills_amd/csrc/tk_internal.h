@@ -49,7 +49,7 @@ inline uint32_t host_substream_key(uint32_t key, uint32_t purpose) {
 struct Config {
   bool nt_stores;           // TK_STORE=nt: non-temporal 16-byte stores
   uint64_t max_blocks;      // TK_MAX_BLOCKS: cap on the grid of the streaming fills
-  int zig_blocks_per_cu;    // TK_ZIG_BLOCKS_PER_CU: persistent grid of the ziggurat pass
+  int unroll;               // TK_UNROLL: 16-byte vectors per lane per tile (1, 2 or 4)
   int choice_blocks_per_cu; // TK_CHOICE_BLOCKS_PER_CU: persistent grid of the choice fill
 };
 const Config &config();

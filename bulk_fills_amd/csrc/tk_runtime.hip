@@ -26,7 +26,7 @@ const Config &config() {
     const char *st = getenv("TK_STORE");
     c.nt_stores = st && strcmp(st, "nt") == 0;
     c.max_blocks = env_u64("TK_MAX_BLOCKS", 0x7FFFFFFFull);
-    c.zig_blocks_per_cu = (int)env_u64("TK_ZIG_BLOCKS_PER_CU", 8);
+    c.unroll = (int)env_u64("TK_UNROLL", 1);
     c.choice_blocks_per_cu = (int)env_u64("TK_CHOICE_BLOCKS_PER_CU", 8);
     return c;
   }();

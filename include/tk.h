@@ -94,8 +94,8 @@ tk_status tk_fill_i64_below(uint32_t key, uint64_t start_draw, uint64_t n, int64
  * taken when below X[layer+1]; the ~0.43 % of draws that miss continue on the
  * per-index substream split(i) of sub(key, "NORM") (wedge test against exp(-x^2/2), or
  * the tail beyond r).  Two kernels: a table pass and a continuation pass over the listed
- * misses; the list and the 16 KiB layer table are per-device library state, ordered
- * across streams by an event.  i < 2^31.
+ * misses; the miss lists and the 16 KiB layer table are per-device library state,
+ * ordered across streams by an event.  i < 2^31.
  * f32 (tandem-sycl, "Design", §Normals; Phobos, §randn): Box-Muller pairs; draw i
  * belongs to pair c = i >> 1 built from the f32 uniforms at words 2c and 2c+1:
  * r = sqrt(-2 ln(1 - u1)), angle 2 pi t with t = u2 wrapped into [-1/2, 1/2); even i
@@ -149,10 +149,12 @@ const char *tk_status_string(tk_status status);
 int tk_last_hip_error(void);
 /* Copies the 1024-layer table the kernels use: x and f of 1025 doubles each (host). */
 tk_status tk_ziggurat_table(double *x, double *f);
-/* Test hook: caps the f64 normal miss list at `capacity` entries on every device (0
- * restores automatic sizing), so the continuation pass's whole-fill walk can be forced.
- * Takes effect at the next tk_fill_normal_f64 call. */
-tk_status tk_debug_set_miss_capacity(uint64_t capacity);
+/* Test hook for the f64 normal's miss lists, applied from the next tk_fill_normal_f64 on
+ * every device: each table-pass work-group keeps at most `per_group` misses (1..16) in its
+ * own slot and sends the rest to an overflow list of `overflow` entries; when that
+ * overflows too, the continuation pass walks the whole fill.  0 restores the default
+ * (16 per group, 65536 overflow entries).  Lets tests force both fallbacks. */
+tk_status tk_debug_set_miss_capacity(uint32_t per_group, uint64_t overflow);
 /* Test hook: waits for the current device's last tk_fill_normal_f64 and returns how many
  * of its draws missed the fast path (synchronous). */
 tk_status tk_debug_last_miss_count(uint64_t *count);

@@ -108,8 +108,9 @@ def test_status_strings():
         s = L.tk_status_string(code).decode()
         assert s.startswith(["TK_OK", "TK_EINVAL", "TK_ERANGE", "TK_ENOMEM", "TK_EHIP"][code])
     assert L.tk_last_hip_error() == 0
-    assert L.tk_debug_set_miss_capacity(1 << 40) == tk.TK_EINVAL
-    assert L.tk_debug_set_miss_capacity(0) == tk.TK_OK
+    assert L.tk_debug_set_miss_capacity(0, 1 << 40) == tk.TK_EINVAL
+    assert L.tk_debug_set_miss_capacity(17, 0) == tk.TK_EINVAL
+    assert L.tk_debug_set_miss_capacity(0, 0) == tk.TK_OK
 
 
 def test_ziggurat_table_is_the_oracles():

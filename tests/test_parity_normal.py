@@ -92,18 +92,19 @@ def test_f64_sampled_misses_at_full_size():
 
 
 def test_f64_forced_list_overflow():
-    """With the list capped far below the miss count the continuation pass walks the
-    whole fill; the result must not change."""
+    """Shrinking the per-group slots pushes misses to the overflow list; shrinking that
+    too makes the continuation pass walk the whole fill.  Neither may change a bit."""
     n = (1 << 20) + 1
     want = run_f64(4, 3, n)
+    total = tk.tk_debug_last_miss_count()
     try:
-        for cap in (1, 16, 1000):
-            tk.tk_debug_set_miss_capacity(cap)
+        for per_group, overflow in ((2, 1 << 22), (1, 1 << 22), (1, 1), (3, 16), (16, 1)):
+            tk.tk_debug_set_miss_capacity(per_group, overflow)
             got = run_f64(4, 3, n)
-            assert np.array_equal(got.view(np.uint64), want.view(np.uint64)), f"cap={cap}"
-            assert tk.tk_debug_last_miss_count() > cap
+            assert np.array_equal(got.view(np.uint64), want.view(np.uint64)), (per_group, overflow)
+            assert tk.tk_debug_last_miss_count() == total, (per_group, overflow)
     finally:
-        tk.tk_debug_set_miss_capacity(0)
+        tk.tk_debug_set_miss_capacity(0, 0)
     check_f64(run_f64(4, 3, n), 4, 3, n, what="after reset")
 
 
