@@ -67,6 +67,7 @@ SIGNATURES = {
     "tk_ziggurat_table": [_p, _p],
     "tk_debug_set_miss_capacity": [_u32, _u64],
     "tk_debug_last_miss_count": [_p],
+    "tk_debug_set_normal_f64_mode": [_u32],
 }
 for _name, _args in SIGNATURES.items():
     _fn = getattr(lib, _name)
@@ -236,6 +237,10 @@ def tk_ziggurat_table():
 
 def tk_debug_set_miss_capacity(per_group, overflow):
     _check(lib.tk_debug_set_miss_capacity(per_group, overflow), "tk_debug_set_miss_capacity")
+
+
+def tk_debug_set_normal_f64_mode(mode):
+    _check(lib.tk_debug_set_normal_f64_mode(mode), "tk_debug_set_normal_f64_mode")
 
 
 def tk_debug_last_miss_count():

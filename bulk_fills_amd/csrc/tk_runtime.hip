@@ -28,6 +28,11 @@ const Config &config() {
     c.max_blocks = env_u64("TK_MAX_BLOCKS", 0x7FFFFFFFull);
     c.unroll = (int)env_u64("TK_UNROLL", 1);
     c.choice_blocks_per_cu = (int)env_u64("TK_CHOICE_BLOCKS_PER_CU", 8);
+    c.zig_tiles = (int)env_u64("TK_ZIG_TILES", 4);
+    const char *zt = getenv("TK_ZIG_TABLE");
+    c.zig_lds = !(zt && strcmp(zt, "global") == 0);
+    const char *zm = getenv("TK_ZIG_MODE");
+    c.zig_fused = !(zm && strcmp(zm, "split") == 0);
     return c;
   }();
   return cfg;

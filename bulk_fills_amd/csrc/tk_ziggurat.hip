@@ -27,6 +27,7 @@
 #include <math.h>
 
 #include <mutex>
+#include <vector>
 
 #include "tk_device.h"
 #include "tk_internal.h"
@@ -34,7 +35,7 @@
 
 namespace tk {
 
-constexpr uint32_t kSlot = 16;  // misses a work-group keeps in its own slot
+constexpr uint32_t kSlotPerTile = 16;  // miss entries a work-group keeps per 4 KiB tile
 
 struct ZigArgs {
   double *out;
@@ -45,64 +46,100 @@ struct ZigArgs {
   uint32_t tail;   // 0 or 1 element after them
   uint32_t hk;     // lowbias32(key)
   uint32_t hkp;    // lowbias32(sub(key, NORM))
-  const double2 *xx;  // {X[L], X[L+1]}, L < 1024
+  const double2 *xx;  // {X[L] * 2^-53, X[L+1]}, L < 1024
   const double *f;    // F[0 .. 1024]
   double r;
   uint32_t ngroups;    // table-pass work-groups = slots
-  uint32_t slot_cap;   // entries used per slot (<= kSlot)
+  uint32_t slot_size;  // entries reserved per slot
+  uint32_t slot_cap;   // entries used per slot (<= slot_size)
   uint32_t *counts;    // [ngroups] misses kept in each slot
-  uint32_t *slots;     // [ngroups * kSlot]
+  uint32_t *slots;     // [ngroups * slot_size]
   uint32_t *ovf;       // overflow list
   uint32_t ovf_cap;
-  uint32_t *ctr;  // [0] overflow entries, [1] finished continuation blocks, [2] last miss total, [3] running total
+  uint32_t *ctr;   // [0] overflow entries (cleared before each fill)
 };
 
-// Fast path of one draw: returns true and the value when u X[L] < X[L+1].
-__device__ __forceinline__ bool zig_fast(const ZigArgs &a, uint32_t lo, uint32_t hi, double *val) {
-  const uint32_t L = lo & 1023u;
-  const double u = unit53_topbits(lo, hi);
-  const double2 e = a.xx[L];
-  const double x = u * e.x;
-  *val = (lo & 1024u) ? -x : x;
+// The fast path of a draw (lo, hi): layer L = lo & 1023, sign bit 10, m = d >> 11 the
+// top 53 bits; x = m * (X[L] 2^-53) equals u * X[L] with u = m 2^-53 bit for bit
+// (scaling by a power of two is exact), and the draw is accepted when x < X[L+1].
+// m is assembled exactly: hi 2^21 + (lo >> 11) < 2^53 in one fused operation.
+__device__ __forceinline__ double zig_x(uint32_t lo, uint32_t hi, double scaled_edge) {
+  const double m = __builtin_fma((double)hi, 0x1p21, (double)(lo >> 11));
+  return m * scaled_edge;
+}
+
+__device__ __forceinline__ bool zig_fast(const double2 *tab, uint32_t lo, uint32_t hi, double *val) {
+  const double2 e = tab[lo & 1023u];
+  const double x = zig_x(lo, hi, e.x);
+  // the sign is bit 10 of the draw, moved to bit 63 (x >= 0, so this is -x when set)
+  *val = __longlong_as_double(__double_as_longlong(x) ^ ((long long)(lo & 1024u) << 53));
   return x < e.y;
 }
 
-// Appends element k to the work-group's queue for every lane with `pred`.  Called by all
-// lanes of the wave.
-__device__ __forceinline__ void enqueue(bool pred, uint32_t k, uint32_t *q, uint32_t *qn, const ZigArgs &a) {
-  const uint64_t m = __ballot(pred);
-  if (m == 0) return;
-  const int leader = __ffsll((unsigned long long)m) - 1;
-  uint32_t base = 0;
-  if (lane_id() == leader) base = atomicAdd(qn, (uint32_t)__popcll(m));
-  base = (uint32_t)__shfl((int)base, leader);
-  if (pred) {
-    const uint32_t rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-    const uint32_t slot = base + rank;
-    if (slot < a.slot_cap) {
-      q[slot] = k;
-    } else {  // the group's slot is full: overflow list
-      const uint32_t g = atomicAdd(&a.ctr[0], 1u);
-      if (g < a.ovf_cap) a.ovf[g] = k;
-    }
+// Stores entry k at position `slot` of the work-group's queue if below `cap`.  Past it, a
+// fused table pass only counts the miss (the group re-walks); the two-kernel pass appends
+// it to the overflow list.
+template <bool kFused>
+__device__ __forceinline__ void queue_put(uint32_t slot, uint32_t k, uint32_t *q, uint32_t cap, const ZigArgs &a) {
+  if (slot < cap) {
+    q[slot] = k;
+  } else if (!kFused) {
+    const uint32_t g = atomicAdd(&a.ctr[0], 1u);
+    if (g < a.ovf_cap) a.ovf[g] = k;
   }
 }
 
-template <int U, bool kNT>
+// Appends the lane's misses (element k0 when p0, k0 + 1 when p1) to the work-group's
+// queue: two ballots, one LDS atomic per wave, ranks from mbcnt.  Called by all lanes of
+// the wave (every lane is active in the table pass).
+template <bool kFused>
+__device__ __forceinline__ void enqueue2(bool p0, bool p1, uint32_t k0, uint32_t *q, uint32_t *qn, uint32_t cap,
+                                         const ZigArgs &a) {
+  const uint64_t m0 = __ballot(p0), m1 = __ballot(p1);
+  if ((m0 | m1) == 0) return;
+  const uint32_t c0 = (uint32_t)__popcll(m0);
+  uint32_t base = 0;
+  if (lane_id() == 0) base = atomicAdd(qn, c0 + (uint32_t)__popcll(m1));
+  base = (uint32_t)__shfl((int)base, 0);
+  if (p0)
+    queue_put<kFused>(base + __builtin_amdgcn_mbcnt_hi((uint32_t)(m0 >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m0, 0u)),
+                      k0, q, cap, a);
+  if (p1)
+    queue_put<kFused>(base + c0 + __builtin_amdgcn_mbcnt_hi((uint32_t)(m1 >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m1, 0u)),
+                      k0 + 1, q, cap, a);
+}
+
+__device__ double zig_slow(const ZigArgs &a, uint64_t k);
+
+// Table pass: T consecutive 4 KiB tiles per work-group.  With kLds the 16 KiB layer table
+// is first copied to LDS (one copy per T tiles) and gathered from there; otherwise the
+// gathers go to the table in device memory through L1/L2.
+// With kFused the work-group finishes its own misses after its stores, while the lines it
+// just wrote are still in L2.  Its queue holds 16 misses per tile (about 2.2 expected); a
+// group that finds more (probability ~1e-10) walks its own elements again and finishes
+// every miss it meets, so nothing leaves the work-group.  Otherwise the queue goes to the
+// group's slot for the continuation pass.
+template <int T, bool kLds, bool kNT, bool kFused>
 __global__ __launch_bounds__(kBlock) void k_zig_table_pass(ZigArgs a) {
-  __shared__ uint32_t q[kSlot];
+  constexpr uint32_t kQueue = kSlotPerTile * T + (kFused ? 2u : 0u);  // fused: + block 0's edge elements
+  __shared__ double2 lds_tab[kLds ? 1024 : 1];
+  __shared__ uint32_t q[kQueue];
   __shared__ uint32_t qn;
+  if (kLds)
+    for (uint32_t i = threadIdx.x; i < 1024; i += kBlock) lds_tab[i] = a.xx[i];
   if (threadIdx.x == 0) qn = 0;
   __syncthreads();
-  const uint64_t v0 = (uint64_t)blockIdx.x * (kBlock * U) + threadIdx.x;
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const uint64_t v = v0 + (uint64_t)u * kBlock;
+  // fused: entries past `cap` are only counted (the group re-walks); two kernels: they go
+  // to the overflow list
+  const uint32_t cap = kFused ? (a.slot_cap < kQueue ? a.slot_cap : kQueue) : a.slot_cap;
+  const double2 *tab = kLds ? lds_tab : a.xx;
+  for (int t = 0; t < T; ++t) {
+    const uint64_t v = ((uint64_t)blockIdx.x * T + t) * kBlock + threadIdx.x;
     const bool in = v < a.nvec;
     const uint32_t c = 2u * (uint32_t)(a.start + a.head + 2 * v);
     double y0, y1;
-    const bool f0 = zig_fast(a, word(a.hk, c), word(a.hk, c + 1), &y0);
-    const bool f1 = zig_fast(a, word(a.hk, c + 2), word(a.hk, c + 3), &y1);
+    const bool f0 = zig_fast(tab, word(a.hk, c), word(a.hk, c + 1), &y0);
+    const bool f1 = zig_fast(tab, word(a.hk, c + 2), word(a.hk, c + 3), &y1);
     if (in) {
       uint4 w;
       w.x = (uint32_t)__double_as_longlong(y0);
@@ -111,9 +148,7 @@ __global__ __launch_bounds__(kBlock) void k_zig_table_pass(ZigArgs a) {
       w.w = (uint32_t)((uint64_t)__double_as_longlong(y1) >> 32);
       store16<kNT>(a.out + a.head + 2 * v, w);
     }
-    const uint32_t k0 = (uint32_t)(a.head + 2 * v);
-    enqueue(in && !f0, k0, q, &qn, a);
-    enqueue(in && !f1, k0 + 1, q, &qn, a);
+    enqueue2<kFused>(in && !f0, in && !f1, (uint32_t)(a.head + 2 * v), q, &qn, cap, a);
   }
   if (blockIdx.x == 0) {  // the element before the first boundary and the one after the last vector
     const uint32_t t = threadIdx.x;
@@ -125,15 +160,42 @@ __global__ __launch_bounds__(kBlock) void k_zig_table_pass(ZigArgs a) {
     if (edge) {
       const uint32_t c = 2u * (uint32_t)(a.start + k);
       double y;
-      fast = zig_fast(a, word(a.hk, c), word(a.hk, c + 1), &y);
+      fast = zig_fast(tab, word(a.hk, c), word(a.hk, c + 1), &y);
       a.out[k] = y;
     }
-    enqueue(edge && !fast, (uint32_t)k, q, &qn, a);
+    enqueue2<kFused>(edge && !fast, false, (uint32_t)k, q, &qn, cap, a);
   }
   __syncthreads();
-  const uint32_t nq = qn < a.slot_cap ? qn : a.slot_cap;
-  if (threadIdx.x == 0) a.counts[blockIdx.x] = nq;
-  if (threadIdx.x < nq) a.slots[(uint64_t)blockIdx.x * kSlot + threadIdx.x] = q[threadIdx.x];
+  const uint32_t total = qn;
+  if (kFused) {
+    if (threadIdx.x == 0) a.counts[blockIdx.x] = total;
+    if (total <= cap) {
+      for (uint32_t j = threadIdx.x; j < total; j += kBlock) {
+        const uint32_t k = q[j];
+        a.out[k] = zig_slow(a, k);
+      }
+    } else {  // more misses than the queue holds: walk the group's elements again
+      const uint64_t e0 = a.head + (uint64_t)blockIdx.x * T * kBlock * 2;
+      uint64_t e1 = e0 + (uint64_t)T * kBlock * 2;
+      if (e1 > a.head + 2 * a.nvec) e1 = a.head + 2 * a.nvec;
+      for (uint64_t k = e0 + threadIdx.x; k < e1; k += kBlock) {
+        const uint32_t c = 2u * (uint32_t)(a.start + k);
+        double y;
+        if (!zig_fast(a.xx, word(a.hk, c), word(a.hk, c + 1), &y)) a.out[k] = zig_slow(a, k);
+      }
+      if (blockIdx.x == 0 && threadIdx.x < 2) {  // and the edge elements
+        const bool has = threadIdx.x == 0 ? a.head != 0 : a.tail != 0;
+        const uint64_t k = threadIdx.x == 0 ? 0 : a.head + 2 * a.nvec;
+        const uint32_t c = 2u * (uint32_t)(a.start + k);
+        double y;
+        if (has && !zig_fast(a.xx, word(a.hk, c), word(a.hk, c + 1), &y)) a.out[k] = zig_slow(a, k);
+      }
+    }
+  } else {
+    const uint32_t nq = total < a.slot_cap ? total : a.slot_cap;
+    if (threadIdx.x == 0) a.counts[blockIdx.x] = nq;
+    for (uint32_t i = threadIdx.x; i < nq; i += kBlock) a.slots[(uint64_t)blockIdx.x * a.slot_size + i] = q[i];
+  }
 }
 
 // Finishes the draw of element k from its primary draw: wedge, tail and restarts all read
@@ -147,7 +209,7 @@ __device__ double zig_slow(const ZigArgs &a, uint64_t k) {
     const uint32_t L = lo & 1023u;
     const bool neg = (lo & 1024u) != 0;
     const double2 e = a.xx[L];
-    const double x = unit53_topbits(lo, hi) * e.x;
+    const double x = zig_x(lo, hi, e.x);
     if (x < e.y) return neg ? -x : x;
     if (L == 0) {  // tail beyond r (Marsaglia & Tsang)
       for (;;) {
@@ -174,55 +236,77 @@ __device__ double zig_slow(const ZigArgs &a, uint64_t k) {
   }
 }
 
-__global__ __launch_bounds__(kBlock) void k_zig_continue(ZigArgs a) {
-  __shared__ uint32_t s_ovf, s_total;
-  if (threadIdx.x == 0) {
-    s_ovf = __hip_atomic_load(&a.ctr[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_total = 0;
+// Exclusive prefix sum of v over the work-group; *total receives the sum.
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *wave_sums, uint32_t *total) {
+  const int lane = lane_id(), w = (int)(threadIdx.x >> 6);
+  uint32_t x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t y = __shfl_up(x, off);
+    if (lane >= off) x += y;
   }
+  if (lane == 63) wave_sums[w] = x;
+  __syncthreads();
+  uint32_t base = 0, sum = 0;
+#pragma unroll
+  for (int i = 0; i < kBlock / 64; ++i) {
+    if (i < w) base += wave_sums[i];
+    sum += wave_sums[i];
+  }
+  *total = sum;
+  return base + x - v;
+}
+
+// Continuation pass.  Block b compacts the misses of table-pass groups
+// [b * gpb, (b + 1) * gpb) (gpb chosen so a block sees about 256 groups' worth of tiles)
+// and spreads them over its lanes, so every lane finishes about two misses.
+__global__ __launch_bounds__(kBlock) void k_zig_continue(ZigArgs a, uint32_t gpb) {
+  __shared__ uint32_t s_ovf;
+  __shared__ uint32_t offs[kBlock + 1];
+  __shared__ uint32_t wave_sums[kBlock / 64];
+  if (threadIdx.x == 0) s_ovf = __hip_atomic_load(&a.ctr[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
   const uint32_t ovf = s_ovf;
-  const uint64_t gid = (uint64_t)blockIdx.x * kBlock + threadIdx.x;
-  const uint64_t stride = (uint64_t)gridDim.x * kBlock;
-  uint32_t mine = 0;
   if (ovf <= a.ovf_cap) {
-    for (uint64_t b = gid; b < a.ngroups; b += stride) {
-      const uint32_t cnt = a.counts[b];
-      mine += cnt;
-      for (uint32_t j = 0; j < cnt; ++j) {
-        const uint32_t k = a.slots[b * kSlot + j];
-        a.out[k] = zig_slow(a, k);
+    const uint64_t g0 = (uint64_t)blockIdx.x * gpb;
+    const uint64_t g = g0 + threadIdx.x;
+    const uint32_t cnt = (threadIdx.x < gpb && g < a.ngroups) ? a.counts[g] : 0u;
+    uint32_t total;
+    const uint32_t off = block_exclusive_scan(cnt, wave_sums, &total);
+    if (threadIdx.x < gpb) offs[threadIdx.x] = off;
+    if (threadIdx.x == 0) offs[gpb] = total;
+    __syncthreads();
+    for (uint32_t m = threadIdx.x; m < total; m += kBlock) {
+      uint32_t lo = 0, hi = gpb;  // the group j with offs[j] <= m < offs[j + 1]
+      while (hi - lo > 1) {
+        const uint32_t mid = (lo + hi) >> 1;
+        if (offs[mid] <= m) lo = mid;
+        else hi = mid;
       }
+      const uint32_t k = a.slots[(g0 + lo) * a.slot_size + (m - offs[lo])];
+      a.out[k] = zig_slow(a, k);
     }
-    for (uint64_t j = gid; j < ovf; j += stride) {
+    const uint64_t gid = (uint64_t)blockIdx.x * kBlock + threadIdx.x;
+    for (uint64_t j = gid; j < ovf; j += (uint64_t)gridDim.x * kBlock) {
       const uint32_t k = a.ovf[j];
       a.out[k] = zig_slow(a, k);
     }
-    if (blockIdx.x == 0 && threadIdx.x == 0) mine += ovf;
   } else {  // the overflow list overflowed: find the misses by walking the whole fill
-    for (uint64_t k = gid; k < a.n; k += stride) {
+    const uint64_t stride = (uint64_t)gridDim.x * kBlock;
+    for (uint64_t k = (uint64_t)blockIdx.x * kBlock + threadIdx.x; k < a.n; k += stride) {
       const uint32_t c = 2u * (uint32_t)(a.start + k);
       double y;
-      if (!zig_fast(a, word(a.hk, c), word(a.hk, c + 1), &y)) {
-        a.out[k] = zig_slow(a, k);
-        ++mine;
-      }
+      if (!zig_fast(a.xx, word(a.hk, c), word(a.hk, c + 1), &y)) a.out[k] = zig_slow(a, k);
     }
   }
-  if (mine) atomicAdd(&s_total, mine);
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    if (s_total) atomicAdd(&a.ctr[3], s_total);
-    __threadfence();
-    const uint32_t done = atomicAdd(&a.ctr[1], 1u);
-    if (done == gridDim.x - 1) {  // every block has read the overflow count: reset for the next fill
-      const uint32_t total = __hip_atomic_load(&a.ctr[3], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(&a.ctr[2], total, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(&a.ctr[3], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(&a.ctr[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(&a.ctr[1], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-  }
+}
+
+// Clears the overflow count before a fill.  A kernel rather than a
+// memset, and no end-of-pass "last block resets" scheme: that needs a device-scope
+// release fence per block, which on MI355X writes back the whole L2 (full of the table
+// pass's output) once per block.
+__global__ void k_zig_reset(uint32_t *ctr) {
+  if (threadIdx.x == 0) ctr[0] = 0u;
 }
 
 // ---------------------------------------------------------------------------------------
@@ -236,9 +320,12 @@ struct ZigDevice {
   uint32_t *ctr = nullptr;
   uint32_t *counts = nullptr;
   uint32_t *slots = nullptr;
-  uint64_t groups_cap = 0;  // slots allocated
+  uint64_t groups_cap = 0;    // counts allocated
+  uint64_t slot_words = 0;    // slot entries allocated
   uint32_t *ovf = nullptr;
   uint64_t ovf_alloc = 0;
+  uint64_t last_groups = 0;   // table-pass groups of the last fill
+  bool last_fused = false;
   hipEvent_t last = nullptr;
   bool recorded = false;
 };
@@ -246,13 +333,14 @@ struct ZigDevice {
 static ZigDevice g_zig[kMaxDevices];
 static std::mutex g_cap_mutex;
 static uint32_t g_debug_slot_cap = 0;
+static int g_debug_mode = 0;  // 0: configured default, 1: two kernels, 2: fused
 static uint64_t g_debug_ovf_cap = 0;
 constexpr uint64_t kOvfDefault = 65536;
 
 static tk_status zig_init(ZigDevice &d) {
   if (d.ready) return TK_OK;
   double2 pairs[TK_ZIG_LAYERS];
-  for (int L = 0; L < TK_ZIG_LAYERS; ++L) pairs[L] = make_double2(tk_zig_x[L], tk_zig_x[L + 1]);
+  for (int L = 0; L < TK_ZIG_LAYERS; ++L) pairs[L] = make_double2(tk_zig_x[L] * 0x1p-53, tk_zig_x[L + 1]);
   if (hipMalloc(&d.xx, sizeof(pairs)) != hipSuccess) return TK_ENOMEM;
   if (hipMalloc(&d.f, sizeof(tk_zig_f)) != hipSuccess) return TK_ENOMEM;
   if (hipMalloc(&d.ctr, 4 * sizeof(uint32_t)) != hipSuccess) return TK_ENOMEM;
@@ -267,18 +355,23 @@ static tk_status zig_init(ZigDevice &d) {
 
 // Grows the slot arrays and the overflow list; the previous fill may still read them, so
 // it is waited for first.
-static tk_status zig_reserve(ZigDevice &d, uint64_t groups, uint64_t ovf_cap) {
-  if (groups <= d.groups_cap && ovf_cap <= d.ovf_alloc) return TK_OK;
+static tk_status zig_reserve(ZigDevice &d, uint64_t groups, uint64_t slot_words, uint64_t ovf_cap) {
+  if (groups <= d.groups_cap && slot_words <= d.slot_words && ovf_cap <= d.ovf_alloc) return TK_OK;
   tk_status st;
   if (d.recorded && (st = hip_status(hipEventSynchronize(d.last))) != TK_OK) return st;
   if (groups > d.groups_cap) {
     if (d.counts) (void)hipFree(d.counts);
-    if (d.slots) (void)hipFree(d.slots);
-    d.counts = d.slots = nullptr;
+    d.counts = nullptr;
     d.groups_cap = 0;
     if (hipMalloc(&d.counts, groups * sizeof(uint32_t)) != hipSuccess) return TK_ENOMEM;
-    if (hipMalloc(&d.slots, groups * kSlot * sizeof(uint32_t)) != hipSuccess) return TK_ENOMEM;
     d.groups_cap = groups;
+  }
+  if (slot_words > d.slot_words) {
+    if (d.slots) (void)hipFree(d.slots);
+    d.slots = nullptr;
+    d.slot_words = 0;
+    if (hipMalloc(&d.slots, slot_words * sizeof(uint32_t)) != hipSuccess) return TK_ENOMEM;
+    d.slot_words = slot_words;
   }
   if (ovf_cap > d.ovf_alloc) {
     if (d.ovf) (void)hipFree(d.ovf);
@@ -290,12 +383,24 @@ static tk_status zig_reserve(ZigDevice &d, uint64_t groups, uint64_t ovf_cap) {
   return TK_OK;
 }
 
-template <int U>
+template <int T, bool kLds, bool kFused>
 static void launch_table_pass(const ZigArgs &a, hipStream_t stream) {
   if (config().nt_stores)
-    hipLaunchKernelGGL((k_zig_table_pass<U, true>), dim3(a.ngroups), dim3(kBlock), 0, stream, a);
+    hipLaunchKernelGGL((k_zig_table_pass<T, kLds, true, kFused>), dim3(a.ngroups), dim3(kBlock), 0, stream, a);
   else
-    hipLaunchKernelGGL((k_zig_table_pass<U, false>), dim3(a.ngroups), dim3(kBlock), 0, stream, a);
+    hipLaunchKernelGGL((k_zig_table_pass<T, kLds, false, kFused>), dim3(a.ngroups), dim3(kBlock), 0, stream, a);
+}
+
+template <bool kFused>
+static void launch_table_pass(int tiles, bool lds, const ZigArgs &a, hipStream_t stream) {
+  switch (tiles) {
+    case 2: lds ? launch_table_pass<2, true, kFused>(a, stream) : launch_table_pass<2, false, kFused>(a, stream); break;
+    case 4: lds ? launch_table_pass<4, true, kFused>(a, stream) : launch_table_pass<4, false, kFused>(a, stream); break;
+    case 8: lds ? launch_table_pass<8, true, kFused>(a, stream) : launch_table_pass<8, false, kFused>(a, stream); break;
+    case 16: lds ? launch_table_pass<16, true, kFused>(a, stream) : launch_table_pass<16, false, kFused>(a, stream); break;
+    case 32: lds ? launch_table_pass<32, true, kFused>(a, stream) : launch_table_pass<32, false, kFused>(a, stream); break;
+    default: launch_table_pass<1, false, kFused>(a, stream); break;
+  }
 }
 
 }  // namespace tk
@@ -323,15 +428,23 @@ tk_status tk_fill_normal_f64(uint32_t key, uint64_t start_draw, uint64_t n, doub
   a.hk = host_lowbias32(key);
   a.hkp = host_substream_key(key, kPurposeNormal64);
   a.r = TK_ZIG_R;
-  const int U = config().unroll == 2 ? 2 : 1;
-  const uint64_t per_group = (uint64_t)kBlock * U;
+  bool fused = config().zig_fused;
+  {
+    std::lock_guard<std::mutex> lock(g_cap_mutex);
+    if (g_debug_mode) fused = g_debug_mode == 2;
+  }
+  const int zt = config().zig_tiles;
+  const int tiles = zt >= 32 ? 32 : zt >= 16 ? 16 : zt >= 8 ? 8 : zt >= 4 ? 4 : zt >= 2 ? 2 : 1;
+  const bool lds = config().zig_lds && tiles > 1;
+  const uint64_t per_group = (uint64_t)kBlock * tiles;
   uint64_t groups = (a.nvec + per_group - 1) / per_group;
   if (groups == 0) groups = 1;
   a.ngroups = (uint32_t)groups;
+  a.slot_size = kSlotPerTile * tiles;
   uint64_t ovf_cap = kOvfDefault;
   {
     std::lock_guard<std::mutex> lock(g_cap_mutex);
-    a.slot_cap = g_debug_slot_cap ? g_debug_slot_cap : kSlot;
+    a.slot_cap = g_debug_slot_cap ? g_debug_slot_cap : a.slot_size;
     if (g_debug_ovf_cap) ovf_cap = g_debug_ovf_cap;
   }
   a.ovf_cap = (uint32_t)ovf_cap;
@@ -339,7 +452,7 @@ tk_status tk_fill_normal_f64(uint32_t key, uint64_t start_draw, uint64_t n, doub
   ZigDevice &d = g_zig[dev];
   std::lock_guard<std::mutex> lock(d.m);
   if ((st = zig_init(d)) != TK_OK) return st;
-  if ((st = zig_reserve(d, groups, ovf_cap)) != TK_OK) return st;
+  if ((st = zig_reserve(d, groups, fused ? 0 : groups * a.slot_size, fused ? 0 : ovf_cap)) != TK_OK) return st;
   if (d.recorded && (st = hip_status(hipStreamWaitEvent(stream, d.last, 0))) != TK_OK) return st;
   a.xx = d.xx;
   a.f = d.f;
@@ -348,16 +461,23 @@ tk_status tk_fill_normal_f64(uint32_t key, uint64_t start_draw, uint64_t n, doub
   a.ovf = d.ovf;
   a.ctr = d.ctr;
 
-  if (U == 2) launch_table_pass<2>(a, stream);
-  else launch_table_pass<1>(a, stream);
-  if ((st = launch_status()) != TK_OK) return st;
-
-  uint64_t cgrid = (groups + kBlock - 1) / kBlock;
-  if (cgrid > 4096) cgrid = 4096;
-  hipLaunchKernelGGL(k_zig_continue, dim3((uint32_t)cgrid), dim3(kBlock), 0, stream, a);
-  if ((st = launch_status()) != TK_OK) return st;
+  if (fused) {
+    launch_table_pass<true>(tiles, lds, a, stream);
+    if ((st = launch_status()) != TK_OK) return st;
+  } else {
+    hipLaunchKernelGGL(k_zig_reset, dim3(1), dim3(64), 0, stream, d.ctr);
+    if ((st = launch_status()) != TK_OK) return st;
+    launch_table_pass<false>(tiles, lds, a, stream);
+    if ((st = launch_status()) != TK_OK) return st;
+    const uint32_t gpb = (uint32_t)(kBlock / tiles);  // table-pass groups per continuation block
+    const uint64_t cgrid = (groups + gpb - 1) / gpb;
+    hipLaunchKernelGGL(k_zig_continue, dim3((uint32_t)cgrid), dim3(kBlock), 0, stream, a, gpb);
+    if ((st = launch_status()) != TK_OK) return st;
+  }
   if ((st = hip_status(hipEventRecord(d.last, stream))) != TK_OK) return st;
   d.recorded = true;
+  d.last_groups = groups;
+  d.last_fused = fused;
   return TK_OK;
 }
 
@@ -371,10 +491,17 @@ tk_status tk_ziggurat_table(double *x, double *f) {
 }
 
 tk_status tk_debug_set_miss_capacity(uint32_t per_group, uint64_t overflow) {
-  if (per_group > kSlot || overflow > 0xFFFFFFFFull) return TK_EINVAL;
+  if (per_group > kSlotPerTile || overflow > 0xFFFFFFFFull) return TK_EINVAL;
   std::lock_guard<std::mutex> lock(g_cap_mutex);
   g_debug_slot_cap = per_group;
   g_debug_ovf_cap = overflow;
+  return TK_OK;
+}
+
+tk_status tk_debug_set_normal_f64_mode(uint32_t mode) {
+  if (mode > 2) return TK_EINVAL;
+  std::lock_guard<std::mutex> lock(g_cap_mutex);
+  g_debug_mode = (int)mode;
   return TK_OK;
 }
 
@@ -390,9 +517,17 @@ tk_status tk_debug_last_miss_count(uint64_t *count) {
     return TK_OK;
   }
   if ((st = hip_status(hipEventSynchronize(d.last))) != TK_OK) return st;
-  uint32_t v = 0;
-  if ((st = hip_status(hipMemcpy(&v, d.ctr + 2, sizeof(v), hipMemcpyDeviceToHost))) != TK_OK) return st;
-  *count = v;
+  // every miss sits in a group's count or, in the two-kernel mode, in the overflow count
+  std::vector<uint32_t> v(d.last_groups);
+  if ((st = hip_status(hipMemcpy(v.data(), d.counts, v.size() * sizeof(uint32_t), hipMemcpyDeviceToHost))) != TK_OK)
+    return st;
+  uint32_t ovf = 0;
+  if (!d.last_fused &&
+      (st = hip_status(hipMemcpy(&ovf, d.ctr, sizeof(uint32_t), hipMemcpyDeviceToHost))) != TK_OK)
+    return st;
+  uint64_t total = ovf;
+  for (uint32_t x : v) total += x;
+  *count = total;
   return TK_OK;
 }
 

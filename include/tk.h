@@ -93,9 +93,10 @@ tk_status tk_fill_i64_below(uint32_t key, uint64_t start_draw, uint64_t n, int64
  * draw d per element: layer d & 1023, sign bit 10, u = (d >> 11) 2^-53; x = u X[layer] is
  * taken when below X[layer+1]; the ~0.43 % of draws that miss continue on the
  * per-index substream split(i) of sub(key, "NORM") (wedge test against exp(-x^2/2), or
- * the tail beyond r).  Two kernels: a table pass and a continuation pass over the listed
- * misses; the miss lists and the 16 KiB layer table are per-device library state,
- * ordered across streams by an event.  i < 2^31.
+ * the tail beyond r).  A table pass writes the fast-path values; the misses are finished
+ * either by the same work-group after its stores or by a continuation pass over a miss
+ * list (tk_debug_set_normal_f64_mode); the lists and the 16 KiB layer table are
+ * per-device library state, ordered across streams by an event.  i < 2^31.
  * f32 (tandem-sycl, "Design", §Normals; Phobos, §randn): Box-Muller pairs; draw i
  * belongs to pair c = i >> 1 built from the f32 uniforms at words 2c and 2c+1:
  * r = sqrt(-2 ln(1 - u1)), angle 2 pi t with t = u2 wrapped into [-1/2, 1/2); even i
@@ -151,10 +152,16 @@ int tk_last_hip_error(void);
 tk_status tk_ziggurat_table(double *x, double *f);
 /* Test hook for the f64 normal's miss lists, applied from the next tk_fill_normal_f64 on
  * every device: each table-pass work-group keeps at most `per_group` misses (1..16) in its
- * own slot and sends the rest to an overflow list of `overflow` entries; when that
- * overflows too, the continuation pass walks the whole fill.  0 restores the default
- * (16 per group, 65536 overflow entries).  Lets tests force both fallbacks. */
+ * queue.  In the two-kernel mode the rest go to an overflow list of `overflow` entries,
+ * and when that overflows too the continuation pass walks the whole fill; in the fused
+ * mode a group with more misses walks its own elements again.  0 restores the defaults
+ * (16 per 4 KiB tile, 65536 overflow entries).  Lets tests force every fallback. */
 tk_status tk_debug_set_miss_capacity(uint32_t per_group, uint64_t overflow);
+/* Test hook: how tk_fill_normal_f64 finishes its misses, from the next call on every
+ * device: 1 = the two-kernel path (table pass, then a continuation pass over the listed
+ * misses), 2 = fused (each table-pass work-group finishes its own misses after its
+ * stores), 0 = the library default.  Both give identical results. */
+tk_status tk_debug_set_normal_f64_mode(uint32_t mode);
 /* Test hook: waits for the current device's last tk_fill_normal_f64 and returns how many
  * of its draws missed the fast path (synchronous). */
 tk_status tk_debug_last_miss_count(uint64_t *count);

@@ -19,6 +19,15 @@ pytestmark = pytest.mark.gpu
 
 TAIL_REL = 1e-12
 F32_ABS = 4e-6
+MODES = {"two_kernels": 1, "fused": 2}
+
+
+@pytest.fixture(params=sorted(MODES))
+def f64_mode(request):
+    """Runs a test once per way of finishing the misses (results must be identical)."""
+    tk.tk_debug_set_normal_f64_mode(MODES[request.param])
+    yield request.param
+    tk.tk_debug_set_normal_f64_mode(0)
 
 
 def check_f64(got, key, start, n=None, draws=None, what=""):
@@ -40,7 +49,7 @@ def run_f64(key, start, n, off=0):
     return b.host(np.float64)
 
 
-def test_f64_small_sweep():
+def test_f64_small_sweep(f64_mode):
     for off in (0, 1):
         for s in (0, 1, 2, 3, 5, 17):
             for n in (1, 2, 3, 5, 16, 17, 255, 4097):
@@ -48,7 +57,7 @@ def test_f64_small_sweep():
 
 
 @pytest.mark.parametrize("key", (1, 2, 3, 0xFFFFFFFF))
-def test_f64_many_tiles_and_miss_count(key):
+def test_f64_many_tiles_and_miss_count(key, f64_mode):
     n = (1 << 20) + 3
     for s in tk_inputs.STARTS:
         for off in (0, 1):
@@ -58,7 +67,7 @@ def test_f64_many_tiles_and_miss_count(key):
             assert tk.tk_debug_last_miss_count() == misses
 
 
-def test_f64_full_2p24_every_element():
+def test_f64_full_2p24_every_element(f64_mode):
     n = 1 << 24
     for s in tk_inputs.STARTS:
         log(f"normal_f64 2^24 start={s}")
@@ -68,7 +77,7 @@ def test_f64_full_2p24_every_element():
         assert abs(misses / n - 0.0042765667) < 5 * np.sqrt(0.0043 / n)
 
 
-def test_f64_full_2p28_sampled():
+def test_f64_full_2p28_sampled(f64_mode):
     n = tk_inputs.FULL_N
     b = DevBuf(n, 8)
     idx = tk_inputs.sample_indices(n, seed=14)
@@ -80,7 +89,7 @@ def test_f64_full_2p28_sampled():
         assert abs(misses - 0.0042765667 * n) < 6 * np.sqrt(0.0043 * n), misses
 
 
-def test_f64_sampled_misses_at_full_size():
+def test_f64_sampled_misses_at_full_size(f64_mode):
     """Every element that leaves the fast path within the first 2^22 of a 2^28 fill."""
     n = tk_inputs.FULL_N
     m = 1 << 22
@@ -92,23 +101,28 @@ def test_f64_sampled_misses_at_full_size():
 
 
 def test_f64_forced_list_overflow():
-    """Shrinking the per-group slots pushes misses to the overflow list; shrinking that
-    too makes the continuation pass walk the whole fill.  Neither may change a bit."""
+    """Two kernels: shrinking the per-group slots pushes misses to the overflow list, and
+    shrinking that too makes the continuation pass walk the whole fill.  Fused: a group
+    whose misses exceed its queue walks its own elements again.  No bit may change."""
     n = (1 << 20) + 1
+    tk.tk_debug_set_normal_f64_mode(2)
     want = run_f64(4, 3, n)
     total = tk.tk_debug_last_miss_count()
     try:
-        for per_group, overflow in ((2, 1 << 22), (1, 1 << 22), (1, 1), (3, 16), (16, 1)):
-            tk.tk_debug_set_miss_capacity(per_group, overflow)
-            got = run_f64(4, 3, n)
-            assert np.array_equal(got.view(np.uint64), want.view(np.uint64)), (per_group, overflow)
-            assert tk.tk_debug_last_miss_count() == total, (per_group, overflow)
+        for mode in (1, 2):  # two kernels: slot -> overflow list -> whole-fill walk; fused: group re-walk
+            tk.tk_debug_set_normal_f64_mode(mode)
+            for per_group, overflow in ((2, 1 << 22), (1, 1 << 22), (1, 1), (3, 16), (16, 1)):
+                tk.tk_debug_set_miss_capacity(per_group, overflow)
+                got = run_f64(4, 3, n)
+                assert np.array_equal(got.view(np.uint64), want.view(np.uint64)), (mode, per_group, overflow)
+                assert tk.tk_debug_last_miss_count() == total, (mode, per_group, overflow)
     finally:
         tk.tk_debug_set_miss_capacity(0, 0)
+        tk.tk_debug_set_normal_f64_mode(0)
     check_f64(run_f64(4, 3, n), 4, 3, n, what="after reset")
 
 
-def test_f64_two_streams_share_the_list():
+def test_f64_two_streams_share_the_list(f64_mode):
     n = (1 << 20) + 7
     streams = [torch.cuda.Stream(), torch.cuda.Stream()]
     bufs = [DevBuf(n, 8) for _ in range(4)]
