@@ -33,9 +33,11 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--warmup-seconds", type=float, default=2.0,
                     help="keep warming up for at least this long (the pages warm each row for 2 s)")
-    ap.add_argument("--cpu-sample-log2", type=int, default=22,
+    ap.add_argument("--cpu-sample-log2", type=int, default=26,
                     help="elements per fill in the oracle's CPU sample (0 disables it)")
-    ap.add_argument("--only", default="", help="comma-separated fill names to run (profiling)")
+    ap.add_argument("--only", default="",
+                    help="comma-separated fill names to run (profiling); 'calib_copy' adds a plain 1 GiB "
+                         "device copy used to calibrate the HBM byte counters")
     return ap.parse_args()
 
 
@@ -48,6 +50,8 @@ def build_step(tk, torch, n):
     tk.tk_fill_normal_f32(ti.DROPOUT_X_KEY, 0, n, x)          # X ~ N(0, 1), seed 7
     table = tk.tk_alias_create(ti.zipf_weights())
     optr = out.data_ptr()
+    # the library finishes ziggurat misses inside the table pass unless told otherwise
+    zig_kernels = 3 if os.environ.get("TK_ZIG_MODE") == "split" else 1
     ks = lambda s: ti.KEYS[s % 3]
     st = lambda s: ti.STARTS[s % 3]
     fills = [
@@ -65,14 +69,35 @@ def build_step(tk, torch, n):
         ("u64_below_2^64-2", 8 * n, 0, 1, lambda s: tk.tk_fill_u64_below(1, 0, n, (1 << 64) - 2, optr)),
         ("i32_below_low", 4 * n, 0, 1, lambda s: tk.tk_fill_i32_below(1, 0, n, ti.LOW, ti.LOW_BOUND, optr)),
         ("i64_below32_low", 8 * n, 0, 1, lambda s: tk.tk_fill_i64_below32(1, 0, n, ti.LOW, ti.LOW_BOUND, optr)),
-        ("normal_f64", 8 * n, 0, 2, lambda s: tk.tk_fill_normal_f64(1, st(s), n, optr)),
+        ("normal_f64", 8 * n, 0, zig_kernels, lambda s: tk.tk_fill_normal_f64(1, st(s), n, optr)),
         ("normal_f32", 4 * n, 0, 1, lambda s: tk.tk_fill_normal_f32(1, 0, n, optr)),
         ("dropout_f32", 4 * n, 4 * n, 1,
          lambda s: tk.tk_dropout_f32(ti.DROPOUT_KEY, 0, n, ti.DROPOUT_P, x.data_ptr(), optr)),
         ("choice_u32", 4 * n, 0, 1, lambda s: tk.tk_fill_choice_u32(1, 0, n, table, optr)),
         ("philox_u32", 4 * n, 0, 1, lambda s: tk.tk_philox_fill_u32(1, st(s), n, optr)),
     ]
-    return fills, (out, x, table)
+    # not a fill: a plain copy of a known size, only when named with --only
+    xc = x.view(torch.uint8)
+    calib = ("calib_copy", 4 * n, 4 * n, 1, lambda s: out[:4 * n].copy_(xc))
+    return fills, calib, (out, x, table)
+
+
+def measured_traffic(fill):
+    """HBM bytes per launch of `fill`'s kernel from the committed rocprofv3 counter record
+    (FETCH_SIZE and WRITE_SIZE scaled by a copy-kernel calibration), or None when there is
+    no record or the kernel's sources changed since the counters were taken."""
+    import hashlib
+    here = os.path.dirname(os.path.abspath(__file__))
+    path = os.path.join(here, "profiles", "hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path)).get("kernels", {}).get(fill)
+    if not rec:
+        return None
+    h = hashlib.sha256()
+    for f in rec["sources"]:
+        h.update(open(os.path.join(here, "bulk_fills_amd", "csrc", f), "rb").read())
+    return rec["traffic_bytes"] if h.hexdigest() == rec["source_sha256"] else None
 
 
 def cpu_baseline(n_sample):
@@ -119,10 +144,10 @@ def main():
     import tk_inputs as ti
 
     n = ti.FULL_N
-    fills, keep = build_step(tk, torch, n)
+    fills, calib, keep = build_step(tk, torch, n)
     if args.only:
         wanted = set(args.only.split(","))
-        fills = [f for f in fills if f[0] in wanted]
+        fills = [f for f in fills + [calib] if f[0] in wanted]
     torch.cuda.synchronize()
 
     def step(s, events=None):
@@ -162,13 +187,15 @@ def main():
                           "min_ms": min(ms), "GiB_per_s": wbytes / (statistics.median(ms) / 1e3) / GIB,
                           "bytes_written": wbytes, "bytes_read": rbytes, "kernels": nk}
     # dominant single-kernel fill: the largest share of the step's device time
-    single = {k: v for k, v in per_fill.items() if v["kernels"] == 1}
+    single = {k: v for k, v in per_fill.items() if v["kernels"] == 1 and k != "calib_copy"}
     dom = max(single, key=lambda k: single[k]["mean_ms"])
     d = per_fill[dom]
     algo_bytes = d["bytes_written"] + d["bytes_read"]
     achieved = algo_bytes / (d["mean_ms"] / 1e3) / 1e9
+    traffic = measured_traffic(dom)
     roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": round(traffic) if traffic is not None else None,
                 "bytes_per_launch": algo_bytes, "avg_launch_ms": round(d["mean_ms"], 5)}
     cpu = cpu_baseline(1 << args.cpu_sample_log2) if args.cpu_sample_log2 > 0 else None
 
