@@ -71,9 +71,26 @@ __device__ __forceinline__ double zig_x(uint32_t lo, uint32_t hi, double scaled_
 __device__ __forceinline__ bool zig_fast(const double2 *tab, uint32_t lo, uint32_t hi, double *val) {
   const double2 e = tab[lo & 1023u];
   const double x = zig_x(lo, hi, e.x);
-  // the sign is bit 10 of the draw, moved to bit 63 (x >= 0, so this is -x when set)
-  *val = __longlong_as_double(__double_as_longlong(x) ^ ((long long)(lo & 1024u) << 53));
+  // the sign is bit 10 of the draw, moved to bit 63 (x >= 0, so this is -x when set):
+  // x_hi ^ ((lo << 21) & 0x80000000) as one v_bitop3 (truth table 0x78 = a ^ (b & c))
+  const uint64_t xb = (uint64_t)__double_as_longlong(x);
+  const uint32_t sh = __builtin_amdgcn_bitop3_b32((uint32_t)(xb >> 32), lo << 21, 0x80000000u, 0x78);
+  *val = __longlong_as_double((long long)(((uint64_t)sh << 32) | (uint32_t)xb));
   return x < e.y;
+}
+
+// The four words of vector v: counters c0 .. c0+3 with c0 = 2 (start + head + 2v).  When
+// start + head is even, c0 is a multiple of 4 and (c0 + j) ^ hk = c0 ^ (hk ^ j), one xor
+// with a uniform value per word.
+template <bool kAligned4>
+__device__ __forceinline__ void zig_words(uint32_t hk, uint32_t c0, uint32_t w[4]) {
+  if (kAligned4) {
+#pragma unroll
+    for (uint32_t j = 0; j < 4; ++j) w[j] = lowbias32(c0 ^ (hk ^ j));
+  } else {
+#pragma unroll
+    for (uint32_t j = 0; j < 4; ++j) w[j] = word(hk, c0 + j);
+  }
 }
 
 // Stores entry k at position `slot` of the work-group's queue if below `cap`.  Past it, a
@@ -95,7 +112,7 @@ __device__ __forceinline__ void queue_put(uint32_t slot, uint32_t k, uint32_t *q
 template <bool kFused>
 __device__ __forceinline__ void enqueue2(bool p0, bool p1, uint32_t k0, uint32_t *q, uint32_t *qn, uint32_t cap,
                                          const ZigArgs &a) {
-  const uint64_t m0 = __ballot(p0), m1 = __ballot(p1);
+  const uint64_t m0 = __builtin_amdgcn_ballot_w64(p0), m1 = __builtin_amdgcn_ballot_w64(p1);
   if ((m0 | m1) == 0) return;
   const uint32_t c0 = (uint32_t)__popcll(m0);
   uint32_t base = 0;
@@ -119,6 +136,47 @@ __device__ double zig_slow(const ZigArgs &a, uint64_t k);
 // group that finds more (probability ~1e-10) walks its own elements again and finishes
 // every miss it meets, so nothing leaves the work-group.  Otherwise the queue goes to the
 // group's slot for the continuation pass.
+// One tile: 256 lanes, two elements each.  kCheck guards vectors past the end (only the
+// last group needs it).
+template <bool kAligned4, bool kCheck, bool kFused, bool kNT>
+__device__ __forceinline__ void zig_tile(const ZigArgs &a, const double2 *tab, uint64_t v, uint32_t *q,
+                                         uint32_t *qn, uint32_t cap) {
+  const bool in = !kCheck || v < a.nvec;
+  uint32_t w[4];
+  zig_words<kAligned4>(a.hk, 2u * (uint32_t)(a.start + a.head + 2 * v), w);
+  double y0, y1;
+  const bool f0 = zig_fast(tab, w[0], w[1], &y0);
+  const bool f1 = zig_fast(tab, w[2], w[3], &y1);
+  if (in) {
+    uint4 o;
+    o.x = (uint32_t)__double_as_longlong(y0);
+    o.y = (uint32_t)((uint64_t)__double_as_longlong(y0) >> 32);
+    o.z = (uint32_t)__double_as_longlong(y1);
+    o.w = (uint32_t)((uint64_t)__double_as_longlong(y1) >> 32);
+    store16<kNT>(a.out + a.head + 2 * v, o);
+  }
+  enqueue2<kFused>(in && !f0, in && !f1, (uint32_t)(a.head + 2 * v), q, qn, cap, a);
+}
+
+template <int T, bool kAligned4, bool kFused, bool kNT>
+__device__ __forceinline__ void zig_tiles(const ZigArgs &a, const double2 *tab, uint32_t *q, uint32_t *qn,
+                                          uint32_t cap) {
+  const uint64_t v0 = (uint64_t)blockIdx.x * T * kBlock + threadIdx.x;
+  if ((uint64_t)(blockIdx.x + 1) * T * kBlock <= a.nvec) {
+    for (int t = 0; t < T; ++t) zig_tile<kAligned4, false, kFused, kNT>(a, tab, v0 + (uint64_t)t * kBlock, q, qn, cap);
+  } else {
+    for (int t = 0; t < T; ++t) zig_tile<kAligned4, true, kFused, kNT>(a, tab, v0 + (uint64_t)t * kBlock, q, qn, cap);
+  }
+}
+
+// Table pass: T consecutive 4 KiB tiles per work-group.  With kLds the 16 KiB layer table
+// is first copied to LDS (one copy per T tiles) and gathered from there; otherwise the
+// gathers go to the table in device memory through L1/L2.
+// With kFused the work-group finishes its own misses after its stores, while the lines it
+// just wrote are still in L2.  Its queue holds 16 misses per tile (about 2.2 expected); a
+// group that finds more (probability ~1e-10) walks its own elements again and finishes
+// every miss it meets, so nothing leaves the work-group.  Otherwise the queue goes to the
+// group's slot for the continuation pass.
 template <int T, bool kLds, bool kNT, bool kFused>
 __global__ __launch_bounds__(kBlock) void k_zig_table_pass(ZigArgs a) {
   constexpr uint32_t kQueue = kSlotPerTile * T + (kFused ? 2u : 0u);  // fused: + block 0's edge elements
@@ -133,23 +191,8 @@ __global__ __launch_bounds__(kBlock) void k_zig_table_pass(ZigArgs a) {
   // to the overflow list
   const uint32_t cap = kFused ? (a.slot_cap < kQueue ? a.slot_cap : kQueue) : a.slot_cap;
   const double2 *tab = kLds ? lds_tab : a.xx;
-  for (int t = 0; t < T; ++t) {
-    const uint64_t v = ((uint64_t)blockIdx.x * T + t) * kBlock + threadIdx.x;
-    const bool in = v < a.nvec;
-    const uint32_t c = 2u * (uint32_t)(a.start + a.head + 2 * v);
-    double y0, y1;
-    const bool f0 = zig_fast(tab, word(a.hk, c), word(a.hk, c + 1), &y0);
-    const bool f1 = zig_fast(tab, word(a.hk, c + 2), word(a.hk, c + 3), &y1);
-    if (in) {
-      uint4 w;
-      w.x = (uint32_t)__double_as_longlong(y0);
-      w.y = (uint32_t)((uint64_t)__double_as_longlong(y0) >> 32);
-      w.z = (uint32_t)__double_as_longlong(y1);
-      w.w = (uint32_t)((uint64_t)__double_as_longlong(y1) >> 32);
-      store16<kNT>(a.out + a.head + 2 * v, w);
-    }
-    enqueue2<kFused>(in && !f0, in && !f1, (uint32_t)(a.head + 2 * v), q, &qn, cap, a);
-  }
+  if (((a.start + a.head) & 1u) == 0) zig_tiles<T, true, kFused, kNT>(a, tab, q, &qn, cap);
+  else zig_tiles<T, false, kFused, kNT>(a, tab, q, &qn, cap);
   if (blockIdx.x == 0) {  // the element before the first boundary and the one after the last vector
     const uint32_t t = threadIdx.x;
     bool edge = false;
