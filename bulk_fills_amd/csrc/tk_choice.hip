@@ -3,7 +3,7 @@
 // tandem-sycl, "Design", §Fills: the choice fill maps each 64-bit draw through an alias
 // table.  The table is built once on the host (Vose's method in integers, so it is exact
 // and reproducible) and uploaded as n pairs {q, alias}.  The fill keeps the table in LDS
-// (one copy per work-group of a persistent grid) and maps draw d to column
+// (one copy per work-group of a few 4 KiB tiles) and maps draw d to column
 // c = (hi32(d) n) >> 32, coin lo32(d): out = coin < q[c] ? c : alias[c].  Four indices
 // leave as one 16-byte store.
 #include <math.h>
@@ -24,7 +24,6 @@ struct tk_alias {
 namespace tk {
 
 constexpr uint32_t kChoiceLdsMax = 8192;  // columns kept in LDS (64 KiB); larger tables are read from L2
-constexpr int kChoiceUnroll = 2;
 
 // Vose's alias construction over integer masses.  Index j owns
 // m_j = floor(w_j / S * n 2^32) of the n 2^32 total; the rounding remainder goes to the
@@ -92,26 +91,43 @@ __device__ __forceinline__ uint32_t choice_elem(const ChoiceArgs &a, const uint2
   return choose<kLds>(a, tab, word(a.hk, c), word(a.hk, c + 1));
 }
 
-template <int U, bool kLds, bool kNT>
-__global__ __launch_bounds__(kBlock) void k_choice(ChoiceArgs a, uint64_t ntiles) {
+// Vector v: four indices from the eight words c0 .. c0+7, c0 = 2 (start + head + 4v).  When
+// start + head is a multiple of 4, c0 is a multiple of 8 and (c0 + j) ^ hk = c0 ^ (hk ^ j).
+template <bool kLds, bool kAligned8, bool kCheck, bool kNT>
+__device__ __forceinline__ void choice_vec(const ChoiceArgs &a, const uint2 *tab, uint64_t v) {
+  if (kCheck && v >= a.nvec) return;
+  const uint32_t c0 = 2u * (uint32_t)(a.start + a.head + 4 * v);
+  uint32_t r[4];
+#pragma unroll
+  for (uint32_t j = 0; j < 4; ++j) {
+    const uint32_t lo = kAligned8 ? lowbias32(c0 ^ (a.hk ^ (2 * j))) : word(a.hk, c0 + 2 * j);
+    const uint32_t hi = kAligned8 ? lowbias32(c0 ^ (a.hk ^ (2 * j + 1))) : word(a.hk, c0 + 2 * j + 1);
+    r[j] = choose<kLds>(a, tab, lo, hi);
+  }
+  store16<kNT>(a.out + a.head + 4 * v, make_uint4(r[0], r[1], r[2], r[3]));
+}
+
+template <int T, bool kLds, bool kAligned8, bool kNT>
+__device__ __forceinline__ void choice_tiles(const ChoiceArgs &a, const uint2 *tab) {
+  const uint64_t v0 = (uint64_t)blockIdx.x * T * kBlock + threadIdx.x;
+  if ((uint64_t)(blockIdx.x + 1) * T * kBlock <= a.nvec) {
+    for (int t = 0; t < T; ++t) choice_vec<kLds, kAligned8, false, kNT>(a, tab, v0 + (uint64_t)t * kBlock);
+  } else {
+    for (int t = 0; t < T; ++t) choice_vec<kLds, kAligned8, true, kNT>(a, tab, v0 + (uint64_t)t * kBlock);
+  }
+}
+
+// T consecutive 4 KiB tiles per work-group over a one-shot grid; with kLds the table is
+// copied to LDS once per group.
+template <int T, bool kLds, bool kNT>
+__global__ __launch_bounds__(kBlock) void k_choice(ChoiceArgs a) {
   extern __shared__ uint2 tab[];
   if (kLds) {
     for (uint32_t i = threadIdx.x; i < a.n; i += kBlock) tab[i] = a.table[i];
     __syncthreads();
   }
-  for (uint64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
-    const uint64_t v0 = tile * (uint64_t)(kBlock * U) + threadIdx.x;
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const uint64_t v = v0 + (uint64_t)u * kBlock;
-      if (v >= a.nvec) continue;
-      const uint32_t c = 2u * (uint32_t)(a.start + a.head + 4 * v);
-      uint32_t r[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) r[j] = choose<kLds>(a, tab, word(a.hk, c + 2 * j), word(a.hk, c + 2 * j + 1));
-      store16<kNT>(a.out + a.head + 4 * v, make_uint4(r[0], r[1], r[2], r[3]));
-    }
-  }
+  if (((a.start + a.head) & 3u) == 0) choice_tiles<T, kLds, true, kNT>(a, tab);
+  else choice_tiles<T, kLds, false, kNT>(a, tab);
   if (blockIdx.x == 0) {
     const uint32_t t = threadIdx.x;
     if (t < a.head) a.out[t] = choice_elem<kLds>(a, tab, t);
@@ -122,13 +138,26 @@ __global__ __launch_bounds__(kBlock) void k_choice(ChoiceArgs a, uint64_t ntiles
   }
 }
 
-template <bool kLds>
-static void launch_choice(const ChoiceArgs &a, uint32_t grid, uint64_t ntiles, hipStream_t stream) {
+template <int T, bool kLds>
+static void launch_choice_t(const ChoiceArgs &a, uint32_t grid, hipStream_t stream) {
   const size_t lds = kLds ? (size_t)a.n * sizeof(uint2) : 0;
   if (config().nt_stores)
-    hipLaunchKernelGGL((k_choice<kChoiceUnroll, kLds, true>), dim3(grid), dim3(kBlock), lds, stream, a, ntiles);
+    hipLaunchKernelGGL((k_choice<T, kLds, true>), dim3(grid), dim3(kBlock), lds, stream, a);
   else
-    hipLaunchKernelGGL((k_choice<kChoiceUnroll, kLds, false>), dim3(grid), dim3(kBlock), lds, stream, a, ntiles);
+    hipLaunchKernelGGL((k_choice<T, kLds, false>), dim3(grid), dim3(kBlock), lds, stream, a);
+}
+
+template <bool kLds>
+static void launch_choice(const ChoiceArgs &a, int tiles, hipStream_t stream) {
+  const uint64_t per_group = (uint64_t)kBlock * tiles;
+  uint64_t groups = (a.nvec + per_group - 1) / per_group;
+  if (groups == 0) groups = 1;
+  switch (tiles) {
+    case 1: launch_choice_t<1, kLds>(a, (uint32_t)groups, stream); break;
+    case 2: launch_choice_t<2, kLds>(a, (uint32_t)groups, stream); break;
+    case 8: launch_choice_t<8, kLds>(a, (uint32_t)groups, stream); break;
+    default: launch_choice_t<4, kLds>(a, (uint32_t)groups, stream); break;
+  }
 }
 
 }  // namespace tk
@@ -222,13 +251,10 @@ tk_status tk_fill_choice_u32(uint32_t key, uint64_t start_draw, uint64_t n, cons
   a.n = table->n;
   a.table = table->table;
 
-  const uint64_t per_tile = (uint64_t)kBlock * kChoiceUnroll;
-  const uint64_t ntiles = (a.nvec + per_tile - 1) / per_tile;
-  uint64_t grid = (uint64_t)device_cus(dev) * (uint64_t)config().choice_blocks_per_cu;
-  if (grid > ntiles) grid = ntiles;
-  if (grid == 0) grid = 1;
-  if (a.n <= kChoiceLdsMax) launch_choice<true>(a, (uint32_t)grid, ntiles, stream);
-  else launch_choice<false>(a, (uint32_t)grid, ntiles, stream);
+  const int zt = config().choice_tiles;
+  const int tiles = zt >= 8 ? 8 : zt >= 4 ? 4 : zt >= 2 ? 2 : 1;
+  if (a.n <= kChoiceLdsMax) launch_choice<true>(a, tiles, stream);
+  else launch_choice<false>(a, tiles, stream);
   return launch_status();
 }
 

@@ -50,7 +50,7 @@ struct Config {
   bool nt_stores;           // TK_STORE=nt: non-temporal 16-byte stores
   uint64_t max_blocks;      // TK_MAX_BLOCKS: cap on the grid of the streaming fills
   int unroll;               // TK_UNROLL: 16-byte vectors per lane per tile (1, 2 or 4)
-  int choice_blocks_per_cu; // TK_CHOICE_BLOCKS_PER_CU: persistent grid of the choice fill
+  int choice_tiles;         // TK_CHOICE_TILES: 4 KiB tiles per choice work-group (1, 2, 4, 8)
   int zig_tiles;            // TK_ZIG_TILES: 4 KiB tiles per ziggurat table-pass work-group (1 or 8)
   bool zig_fused;           // TK_ZIG_MODE=fused|split: misses finished in the table pass, or in a second kernel
   bool zig_lds;             // TK_ZIG_TABLE=lds|global: where the table pass gathers the layers
