@@ -108,6 +108,8 @@ fill_f32 = _simple("orc_fill_f32", np.float32, _fp)
 fill_f64 = _simple("orc_fill_f64", np.float64, _dp)
 fill_bool = _simple("orc_fill_bool", np.uint8, _u8p)
 fill_normal_f32 = _simple("orc_fill_normal_f32", np.float32, _fp)
+fill_exponential_f64 = _simple("orc_fill_exponential_f64", np.float64, _dp)
+fill_exponential_f32 = _simple("orc_fill_exponential_f32", np.float32, _fp)
 philox_fill_u32 = _simple("orc_philox_fill_u32", np.uint32, _u32p, C.c_uint64)
 philox_fill_u64 = _simple("orc_philox_fill_u64", np.uint64, _u64p, C.c_uint64)
 philox_fill_f32 = _simple("orc_philox_fill_f32", np.float32, _fp, C.c_uint64)

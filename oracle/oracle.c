@@ -417,6 +417,41 @@ int orc_fill_normal_f32(uint32_t key, uint64_t start, uint64_t n, const uint64_t
 }
 
 /* ---------------------------------------------------------------------------------
+ * Exponentials.  tandem-sycl, "Design", §Exponentials and tandem-cuda, "Performance",
+ * §GPU: the f32 exponential keeps every draw within 0.571 ulp so that 1 - exp(-x) maps
+ * back to the draw's own 2^-24 grid point; the f64 one uses an f64 logarithm.
+ * READING: x = -ln(1 - u) (inversion), +0.0 at u = 0.
+ *   f64: u = the f64 uniform of the draw, (d & (2^53 - 1)) * 2^-53, x in f64.
+ *   f32: u = (word & 0xFFFFFF) * 2^-24 (the low 24 bits), x = -ln(1 - u) rounded once to
+ *        f32 (evaluated in f64; 1 - u is exact in both).
+ * ------------------------------------------------------------------------------- */
+static double neg_log1m(double u)
+{
+    double l = log(1.0 - u);
+    return l == 0.0 ? 0.0 : -l;
+}
+
+int orc_fill_exponential_f64(uint32_t key, uint64_t start, uint64_t n, const uint64_t *draws, double *out)
+{
+    CHECK(MAX_DRAW_W64);
+    for (uint64_t k = 0; k < n; ++k) {
+        uint64_t d = draw64(key, (uint32_t)DRAW(k));
+        out[k] = neg_log1m((double)(d & ((1ull << 53) - 1u)) * 0x1p-53);
+    }
+    return ORC_OK;
+}
+
+int orc_fill_exponential_f32(uint32_t key, uint64_t start, uint64_t n, const uint64_t *draws, float *out)
+{
+    CHECK(MAX_DRAW_W32);
+    for (uint64_t k = 0; k < n; ++k) {
+        uint32_t w = orc_word(key, (uint32_t)DRAW(k));
+        out[k] = (float)neg_log1m((double)(w & 0xFFFFFFu) * 0x1p-24);
+    }
+    return ORC_OK;
+}
+
+/* ---------------------------------------------------------------------------------
  * Dropout.  Phobos, §dropout: where(uniform(seed, counter) >= p, x / (1 - p), 0) with
  * p in [0, 1); the counter is the element's flat index.  1 - p and the quotient are f32
  * operations (a true division, not a multiply by a reciprocal).

@@ -85,6 +85,13 @@ int orc_fill_normal_f64(uint32_t key, uint64_t start, uint64_t n, const uint64_t
 int orc_fill_normal_f32(uint32_t key, uint64_t start, uint64_t n, const uint64_t *draws,
                         float *out);
 
+/* Exponentials: x = -ln(1 - u); f64 from the f64 uniform, f32 from a 2^-24 grid (rounded
+ * once from f64). */
+int orc_fill_exponential_f64(uint32_t key, uint64_t start, uint64_t n, const uint64_t *draws,
+                             double *out);
+int orc_fill_exponential_f32(uint32_t key, uint64_t start, uint64_t n, const uint64_t *draws,
+                             float *out);
+
 /* Dropout: y[k] = u >= p ? x[k] / (1 - p) : 0, u the uniform at draw d_k. */
 int orc_dropout_f32(uint32_t key, uint64_t start, uint64_t n, const uint64_t *draws, float p,
                     const float *x, float *y, uint8_t *mask);

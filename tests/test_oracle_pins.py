@@ -203,6 +203,7 @@ FILLS = {
     "i64_below32": lambda k, s, n, draws=None: oracle.fill_i64_below32(k, s, n, -500, 1000, draws=draws),
     "i64_below": lambda k, s, n, draws=None: oracle.fill_i64_below(k, s, n, -(1 << 40), 1 << 41, draws=draws),
     "philox_u32": oracle.philox_fill_u32, "philox_f64": oracle.philox_fill_f64,
+    "exponential_f64": oracle.fill_exponential_f64, "exponential_f32": oracle.fill_exponential_f32,
 }
 
 
@@ -609,3 +610,66 @@ def test_philox_layout_and_statistics():
     hi = oracle.philox_fill_u32(1, 4 << 32, 4)
     lo = oracle.philox_fill_u32(1, 0, 4)
     assert not np.array_equal(hi, lo)
+
+
+# ---------------------------------------------------------------------------------------
+# Exponentials (tandem-sycl "Design" §Exponentials; tandem-cuda "Performance" §GPU: the
+# f32 exponential stays within 0.571 ulp so that 1 - exp(-x) maps back to the draw's own
+# 2^-24 grid point)
+# ---------------------------------------------------------------------------------------
+
+def _inverse_hash_np(y):
+    """Vectorised inverse of lowbias32 over uint64 arrays holding u32 values."""
+    M = np.uint64(M32)
+
+    def unxorshift(v, s):
+        r = v.copy()
+        for _ in range(32 // s + 1):
+            r = v ^ (r >> np.uint64(s))
+        return r & M
+
+    inv2 = np.uint64(pow(PHOBOS["hash_mul_2"] & M32, -1, 1 << 32))
+    inv1 = np.uint64(pow(PHOBOS["hash_mul_1"] & M32, -1, 1 << 32))
+    y = unxorshift(y, 16)
+    y = (y * inv2) & M
+    y = unxorshift(y, 15)
+    y = (y * inv1) & M
+    return unxorshift(y, 16)
+
+
+def test_exponential_f32_every_grid_point():
+    """For every m < 2^24 build the counter whose word has low bits m (inverse hash), and
+    check the oracle's x against the correctly rounded -ln(1 - m 2^-24) (long double) and
+    the page's property that 1 - exp(-x) rounds back to m on the 2^-24 grid."""
+    key = 11
+    m = np.arange(1 << 24, dtype=np.uint64)
+    counters = _inverse_hash_np(m) ^ np.uint64(oracle.hash32(key))
+    x = oracle.fill_exponential_f32(key, 0, 0, draws=counters)
+    assert np.array_equal(oracle.fill_u32(key, 0, 0, draws=counters[:4096]) & 0xFFFFFF, m[:4096].astype(np.uint32))
+    u = m.astype(np.longdouble) * np.longdouble(2.0) ** -24
+    exact = -np.log1p(-u)
+    assert np.array_equal(x, exact.astype(np.float32))
+    back = np.rint((-np.expm1(-x.astype(np.longdouble))) * np.longdouble(2.0) ** 24)
+    assert np.array_equal(back.astype(np.uint64), m)
+    assert x[0] == 0 and not np.signbit(x[0])
+
+
+def test_exponential_f64_accuracy_and_law():
+    import mpmath as mp
+    mp.mp.dps = 40
+    d = oracle.fill_u64(2, 0, 2000)
+    x = oracle.fill_exponential_f64(2, 0, 2000)
+    for di, xi in zip(d[:2000], x[:2000]):
+        uu = mp.mpf(int(di) & ((1 << 53) - 1)) * mp.mpf(2) ** -53
+        ref = -mp.log(1 - uu)
+        if xi == 0:
+            assert ref == 0
+            continue
+        assert abs(mp.mpf(xi) - ref) <= mp.mpf(np.spacing(xi)), (di, xi)
+    n = 1 << 22
+    rng = np.random.default_rng(6)
+    z = oracle.fill_exponential_f64(1, 0, 0, draws=rng.integers(0, 1 << 31, n, dtype=np.uint64))
+    assert abs(z.mean() - 1) < 5 / math.sqrt(n) and abs(z.var() - 1) < 5 * math.sqrt(8 / n)
+    assert stats.kstest(z[: 1 << 20], "expon").pvalue > 1e-4
+    f = oracle.fill_exponential_f32(1, 0, 0, draws=rng.integers(0, 1 << 32, n, dtype=np.uint64))
+    assert abs(f.mean() - 1) < 5 / math.sqrt(n) and f.min() >= 0
