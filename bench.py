@@ -76,10 +76,15 @@ def build_step(tk, torch, n):
         ("choice_u32", 4 * n, 0, 1, lambda s: tk.tk_fill_choice_u32(1, 0, n, table, optr)),
         ("philox_u32", 4 * n, 0, 1, lambda s: tk.tk_philox_fill_u32(1, st(s), n, optr)),
     ]
+    # rows beyond the hot path, timed after it and not counted in `value`
+    next_rows = [
+        ("exponential_f64", 8 * n, 0, 1, lambda s: tk.tk_fill_exponential_f64(ks(s), st(s), n, optr)),
+        ("exponential_f32", 4 * n, 0, 1, lambda s: tk.tk_fill_exponential_f32(ks(s), st(s), n, optr)),
+    ]
     # not a fill: a plain copy of a known size, only when named with --only
     xc = x.view(torch.uint8)
     calib = ("calib_copy", 4 * n, 4 * n, 1, lambda s: out[:4 * n].copy_(xc))
-    return fills, calib, (out, x, table)
+    return fills, next_rows, calib, (out, x, table)
 
 
 def measured_traffic(fill):
@@ -144,10 +149,11 @@ def main():
     import tk_inputs as ti
 
     n = ti.FULL_N
-    fills, calib, keep = build_step(tk, torch, n)
+    fills, next_rows, calib, keep = build_step(tk, torch, n)
     if args.only:
         wanted = set(args.only.split(","))
-        fills = [f for f in fills + [calib] if f[0] in wanted]
+        fills = [f for f in fills + next_rows + [calib] if f[0] in wanted]
+        next_rows = []
     torch.cuda.synchronize()
 
     def step(s, events=None):
@@ -197,6 +203,21 @@ def main():
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": round(traffic) if traffic is not None else None,
                 "bytes_per_launch": algo_bytes, "avg_launch_ms": round(d["mean_ms"], 5)}
+    # rows beyond the hot path: same protocol, separate loop
+    nxt = {}
+    for name, wbytes, _, _, fn in next_rows:
+        for s in range(3):
+            fn(s)
+        ms = []
+        for s in range(K):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn(s)
+            b.record()
+            b.synchronize()
+            ms.append(a.elapsed_time(b))
+        med = statistics.median(ms)
+        nxt[name] = {"GiB_per_s": round(wbytes / (med / 1e3) / GIB, 1), "median_ms": round(med, 4)}
     cpu = cpu_baseline(1 << args.cpu_sample_log2) if args.cpu_sample_log2 > 0 else None
 
     rec = {
@@ -213,6 +234,7 @@ def main():
         "cpu_baseline": cpu,
         "fills": {k: {"GiB_per_s": round(v["GiB_per_s"], 1), "median_ms": round(v["median_ms"], 4),
                       "min_ms": round(v["min_ms"], 4)} for k, v in per_fill.items()},
+        "next_rows": nxt,
         "device": torch.cuda.get_device_name(0),
     }
     print(json.dumps(rec), flush=True)

@@ -54,6 +54,8 @@ SIGNATURES = {
     "tk_fill_i64_below": [_u32, _u64, _u64, _i64, _u64, _p, _p],
     "tk_fill_normal_f64": [_u32, _u64, _u64, _p, _p],
     "tk_fill_normal_f32": [_u32, _u64, _u64, _p, _p],
+    "tk_fill_exponential_f64": [_u32, _u64, _u64, _p, _p],
+    "tk_fill_exponential_f32": [_u32, _u64, _u64, _p, _p],
     "tk_dropout_f32": [_u32, _u64, _u64, _f32, _p, _p, _p, _p],
     "tk_alias_create": [_p, _u32, _p],
     "tk_alias_destroy": [_p],
@@ -141,6 +143,8 @@ tk_fill_f64 = _fill("tk_fill_f64", 8)
 tk_fill_bool = _fill("tk_fill_bool", 1)
 tk_fill_normal_f64 = _fill("tk_fill_normal_f64", 8)
 tk_fill_normal_f32 = _fill("tk_fill_normal_f32", 4)
+tk_fill_exponential_f64 = _fill("tk_fill_exponential_f64", 8)
+tk_fill_exponential_f32 = _fill("tk_fill_exponential_f32", 4)
 tk_philox_fill_u32 = _fill("tk_philox_fill_u32", 4)
 tk_philox_fill_u64 = _fill("tk_philox_fill_u64", 8)
 tk_philox_fill_f32 = _fill("tk_philox_fill_f32", 4)

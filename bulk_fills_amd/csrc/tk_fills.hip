@@ -297,6 +297,46 @@ struct OpNormalF32 : FillBase<float> {
 };
 
 // ---------------------------------------------------------------------------------------
+// Exponentials: x = -ln(1 - u), +0 at u = 0.  The logarithm is the f64 one for both
+// types: rounding it once to f32 gives the correctly rounded value at every point of the
+// f32 fill's 2^-24 grid (checked exhaustively on MI355X; the f32 logf is up to 2 ulp off).
+// ---------------------------------------------------------------------------------------
+__device__ __forceinline__ double neg_log1m(double u) {
+  const double l = log(1.0 - u);
+  return l == 0.0 ? 0.0 : -l;
+}
+
+// f64: u = (d & (2^53 - 1)) 2^-53 of the 64-bit draw.
+struct OpExpF64 : FillBase<uint64_t> {
+  uint32_t hk;
+  __device__ __forceinline__ uint64_t one(uint32_t lo, uint32_t hi) const {
+    return (uint64_t)__double_as_longlong(neg_log1m(unit53_lowbits(lo, hi)));
+  }
+  __device__ __forceinline__ uint64_t elem(uint64_t k) const {
+    const uint32_t c = 2u * (uint32_t)(start + k);
+    return one(word(hk, c), word(hk, c + 1));
+  }
+  __device__ __forceinline__ uint4 vec(uint64_t v) const {
+    const uint32_t c = 2u * (uint32_t)vec_draw(v);
+    const uint64_t a = one(word(hk, c), word(hk, c + 1)), b = one(word(hk, c + 2), word(hk, c + 3));
+    return u4(lo32(a), hi32(a), lo32(b), hi32(b));
+  }
+};
+
+// f32: u = (w & 0xFFFFFF) 2^-24, evaluated in f64 and rounded once.
+struct OpExpF32 : FillBase<uint32_t> {
+  uint32_t hk;
+  __device__ __forceinline__ uint32_t one(uint32_t w) const {
+    return __float_as_uint((float)neg_log1m((double)(w & 0xFFFFFFu) * 0x1p-24));
+  }
+  __device__ __forceinline__ uint32_t elem(uint64_t k) const { return one(word(hk, (uint32_t)(start + k))); }
+  __device__ __forceinline__ uint4 vec(uint64_t v) const {
+    const uint32_t c = (uint32_t)vec_draw(v);
+    return u4(one(word(hk, c)), one(word(hk, c + 1)), one(word(hk, c + 2)), one(word(hk, c + 3)));
+  }
+};
+
+// ---------------------------------------------------------------------------------------
 // Fused dropout: y = u >= p ? x / (1 - p) : +0 (IEEE f32 division), optional mask bytes
 // ---------------------------------------------------------------------------------------
 struct OpDropout : FillBase<float> {
@@ -568,6 +608,20 @@ tk_status tk_fill_normal_f32(uint32_t key, uint64_t start_draw, uint64_t n, floa
   OpNormalF32 op{};
   op.hk = host_lowbias32(key);
   return run_simple(op, out, start_draw, n, stream);
+}
+
+tk_status tk_fill_exponential_f64(uint32_t key, uint64_t start_draw, uint64_t n, double *out, hipStream_t stream) {
+  TK_PRECHECK(out, kMaxW64);
+  OpExpF64 op{};
+  op.hk = host_lowbias32(key);
+  return run_simple(op, (uint64_t *)out, start_draw, n, stream);
+}
+
+tk_status tk_fill_exponential_f32(uint32_t key, uint64_t start_draw, uint64_t n, float *out, hipStream_t stream) {
+  TK_PRECHECK(out, kMaxW32);
+  OpExpF32 op{};
+  op.hk = host_lowbias32(key);
+  return run_simple(op, (uint32_t *)out, start_draw, n, stream);
 }
 
 tk_status tk_dropout_f32(uint32_t key, uint64_t start_draw, uint64_t n, float p, const float *x, float *y,

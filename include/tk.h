@@ -104,6 +104,17 @@ tk_status tk_fill_i64_below(uint32_t key, uint64_t start_draw, uint64_t n, int64
 tk_status tk_fill_normal_f64(uint32_t key, uint64_t start_draw, uint64_t n, double *out, hipStream_t stream);
 tk_status tk_fill_normal_f32(uint32_t key, uint64_t start_draw, uint64_t n, float *out, hipStream_t stream);
 
+/* ---- Exponentials ------------------------------------------------------------------
+ * tandem-sycl, "Design", §Exponentials; tandem-cuda, "Performance", §GPU (the f32
+ * exponential maps 1 - exp(-x) back to the draw's own 2^-24 grid point).  x = -ln(1 - u),
+ * +0.0 at u = 0, by inversion of the draw's uniform:
+ *   f64: u = (u64 draw & (2^53 - 1)) 2^-53; x from the device f64 logarithm (within
+ *        1 ulp of the exact value).                                      (i < 2^31)
+ *   f32: u = (word i & 0xFFFFFF) 2^-24; x correctly rounded to f32 (evaluated in f64 and
+ *        rounded once, which is exact at every one of the 2^24 grid points).  (i < 2^32) */
+tk_status tk_fill_exponential_f64(uint32_t key, uint64_t start_draw, uint64_t n, double *out, hipStream_t stream);
+tk_status tk_fill_exponential_f32(uint32_t key, uint64_t start_draw, uint64_t n, float *out, hipStream_t stream);
+
 /* ---- Fused dropout ------------------------------------------------------------------
  * Phobos, §dropout: y[k] = uniform(key, start_draw + k) >= p ? x[k] / (1 - p) : +0.0, with
  * 1 - p and the quotient rounded as f32 operations (a true division).  p must lie in

@@ -44,7 +44,8 @@ U32MAX = (1 << 32) - 1
 SIMPLE = [("tk_fill_u8", 1, 1 << 34), ("tk_fill_u16", 2, 1 << 33), ("tk_fill_u32", 4, 1 << 32),
           ("tk_fill_u64", 8, 1 << 31), ("tk_fill_f16_bits", 2, 1 << 33), ("tk_fill_f32", 4, 1 << 32),
           ("tk_fill_f64", 8, 1 << 31), ("tk_fill_bool", 1, 1 << 37), ("tk_fill_normal_f64", 8, 1 << 31),
-          ("tk_fill_normal_f32", 4, 1 << 32)]
+          ("tk_fill_normal_f32", 4, 1 << 32), ("tk_fill_exponential_f64", 8, 1 << 31),
+          ("tk_fill_exponential_f32", 4, 1 << 32)]
 
 
 @pytest.mark.parametrize("name,size,limit", SIMPLE)
