@@ -14,6 +14,7 @@
 // the last lane of a wave computes it itself.  No LDS staging and no extra HBM traffic.
 #include "tk_device.h"
 #include "tk_internal.h"
+#include "tk_log.h"
 
 namespace tk {
 
@@ -297,20 +298,16 @@ struct OpNormalF32 : FillBase<float> {
 };
 
 // ---------------------------------------------------------------------------------------
-// Exponentials: x = -ln(1 - u), +0 at u = 0.  The logarithm is the f64 one for both
-// types: rounding it once to f32 gives the correctly rounded value at every point of the
-// f32 fill's 2^-24 grid (checked exhaustively on MI355X; the f32 logf is up to 2 ulp off).
+// Exponentials: x = -ln(1 - u), +0 at u = 0, by inversion of the uniform draw.  1 - u is
+// exact in f64 for both types and the logarithm is tk_log.h's (at most 0.514 ulp); the
+// f32 fill rounds it once, which gives the correctly rounded f32 at every point of its
+// 2^-24 grid.
 // ---------------------------------------------------------------------------------------
-__device__ __forceinline__ double neg_log1m(double u) {
-  const double l = log(1.0 - u);
-  return l == 0.0 ? 0.0 : -l;
-}
-
 // f64: u = (d & (2^53 - 1)) 2^-53 of the 64-bit draw.
 struct OpExpF64 : FillBase<uint64_t> {
   uint32_t hk;
   __device__ __forceinline__ uint64_t one(uint32_t lo, uint32_t hi) const {
-    return (uint64_t)__double_as_longlong(neg_log1m(unit53_lowbits(lo, hi)));
+    return (uint64_t)__double_as_longlong(neg_ln_unit(1.0 - unit53_lowbits(lo, hi)));
   }
   __device__ __forceinline__ uint64_t elem(uint64_t k) const {
     const uint32_t c = 2u * (uint32_t)(start + k);
@@ -323,11 +320,11 @@ struct OpExpF64 : FillBase<uint64_t> {
   }
 };
 
-// f32: u = (w & 0xFFFFFF) 2^-24, evaluated in f64 and rounded once.
+// f32: u = (w & 0xFFFFFF) 2^-24.
 struct OpExpF32 : FillBase<uint32_t> {
   uint32_t hk;
   __device__ __forceinline__ uint32_t one(uint32_t w) const {
-    return __float_as_uint((float)neg_log1m((double)(w & 0xFFFFFFu) * 0x1p-24));
+    return __float_as_uint((float)neg_ln_unit(1.0 - (double)(w & 0xFFFFFFu) * 0x1p-24));
   }
   __device__ __forceinline__ uint32_t elem(uint64_t k) const { return one(word(hk, (uint32_t)(start + k))); }
   __device__ __forceinline__ uint4 vec(uint64_t v) const {
