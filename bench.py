@@ -77,9 +77,16 @@ def build_step(tk, torch, n):
         ("philox_u32", 4 * n, 0, 1, lambda s: tk.tk_philox_fill_u32(1, st(s), n, optr)),
     ]
     # rows beyond the hot path, timed after it and not counted in `value`
+    m20, m24 = 1 << 20, 1 << 24
     next_rows = [
         ("exponential_f64", 8 * n, 0, 1, lambda s: tk.tk_fill_exponential_f64(ks(s), st(s), n, optr)),
         ("exponential_f32", 4 * n, 0, 1, lambda s: tk.tk_fill_exponential_f32(ks(s), st(s), n, optr)),
+        ("dropout_backward_f32", 4 * n, 4 * n, 1,
+         lambda s: tk.tk_dropout_backward_f32(ti.DROPOUT_KEY, 0, n, ti.DROPOUT_P, x.data_ptr(), optr)),
+        # short fills (latency rows: 4 MiB and 8 MiB sit in the caches)
+        ("u32_2^20", 4 * m20, 0, 1, lambda s: tk.tk_fill_u32(1, 0, m20, optr)),
+        ("normal_f64_2^20", 8 * m20, 0, zig_kernels, lambda s: tk.tk_fill_normal_f64(1, st(s), m20, optr)),
+        ("normal_f64_2^24", 8 * m24, 0, zig_kernels, lambda s: tk.tk_fill_normal_f64(1, st(s), m24, optr)),
     ]
     # not a fill: a plain copy of a known size, only when named with --only
     xc = x.view(torch.uint8)
@@ -217,7 +224,8 @@ def main():
             b.synchronize()
             ms.append(a.elapsed_time(b))
         med = statistics.median(ms)
-        nxt[name] = {"GiB_per_s": round(wbytes / (med / 1e3) / GIB, 1), "median_ms": round(med, 4)}
+        nxt[name] = {"GiB_per_s": round(wbytes / (med / 1e3) / GIB, 1), "median_ms": round(med, 4),
+                     "median_us": round(med * 1e3, 1)}
     cpu = cpu_baseline(1 << args.cpu_sample_log2) if args.cpu_sample_log2 > 0 else None
 
     rec = {

@@ -57,6 +57,7 @@ SIGNATURES = {
     "tk_fill_exponential_f64": [_u32, _u64, _u64, _p, _p],
     "tk_fill_exponential_f32": [_u32, _u64, _u64, _p, _p],
     "tk_dropout_f32": [_u32, _u64, _u64, _f32, _p, _p, _p, _p],
+    "tk_dropout_backward_f32": [_u32, _u64, _u64, _f32, _p, _p, _p],
     "tk_alias_create": [_p, _u32, _p],
     "tk_alias_destroy": [_p],
     "tk_alias_export": [_p, _p, _p],
@@ -180,6 +181,12 @@ def tk_dropout_f32(key, start_draw, n, p, x, y, mask=None, stream=None):
     _check(lib.tk_dropout_f32(key, start_draw, n, p, _buf(x, 4, n, "tk_dropout_f32"),
                               _buf(y, 4, n, "tk_dropout_f32"), _buf(mask, 1, n, "tk_dropout_f32"),
                               _stream(stream, y)), "tk_dropout_f32")
+
+
+def tk_dropout_backward_f32(key, start_draw, n, p, dy, dx, stream=None):
+    _check(lib.tk_dropout_backward_f32(key, start_draw, n, p, _buf(dy, 4, n, "tk_dropout_backward_f32"),
+                                       _buf(dx, 4, n, "tk_dropout_backward_f32"), _stream(stream, dx)),
+           "tk_dropout_backward_f32")
 
 
 class Alias:

@@ -9,31 +9,22 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "tk_device_api.h"
+
 namespace tk {
 
 constexpr int kBlock = 256;  // work-group size: four wave64s
 
-// ---- lowbias32 (Phobos stdlib, "Random numbers", §hash32) -----------------------------
-// Three logical xorshifts and two wrapping 32-bit multiplies; the multipliers are the
-// page's i32 constants 2146121005 and -2073254261 as u32 bit patterns.
-__device__ __forceinline__ uint32_t lowbias32(uint32_t x) {
-  x ^= x >> 16;
-  x *= 0x7FEB352Du;
-  x ^= x >> 15;
-  x *= 0x846CA68Bu;
-  x ^= x >> 16;
-  return x;
-}
+// ---- generator and f32 uniform: the public per-element API (include/tk_device_api.h),
+// so that the fills and kernels written against that header draw the same values ------
+__device__ __forceinline__ uint32_t lowbias32(uint32_t x) { return tk_hash32(x); }
 
 // Word c of the stream keyed by hk = lowbias32(key) (Phobos, §uniform: counter ^ hash(seed)).
-__device__ __forceinline__ uint32_t word(uint32_t hk, uint32_t c) { return lowbias32(c ^ hk); }
+__device__ __forceinline__ uint32_t word(uint32_t hk, uint32_t c) { return tk_word(hk, c); }
 
 // ---- exact uniform transforms ---------------------------------------------------------
-// f32: (w & 0x7FFFFF) * 2^-23 built as the float 1.m minus 1 (exact: both are on the
-// 2^-23 grid of [1, 2)).
-__device__ __forceinline__ float unit23(uint32_t w) {
-  return __uint_as_float((w & 0x7FFFFFu) | 0x3F800000u) - 1.0f;
-}
+// f32: (w & 0x7FFFFF) * 2^-23 (exact).
+__device__ __forceinline__ float unit23(uint32_t w) { return tk_unit23(w); }
 
 // f64: (d & (2^53-1)) * 2^-53 from the two words: hi's low 21 bits scaled by 2^-21 plus
 // lo scaled by 2^-53.  Both terms and their sum are exact.

@@ -260,19 +260,12 @@ struct OpBelow64 : FillBase<T> {
 // ---------------------------------------------------------------------------------------
 struct OpNormalF32 : FillBase<float> {
   uint32_t hk;
-  // r = sqrt(-2 ln(1 - u1)) with the hardware base-2 logarithm (ln x = ln 2 * log2 x) and
-  // square root; cos and sin of 2 pi t with the hardware sine and cosine, which take
-  // their argument in turns, so the wrapped t in [-1/2, 1/2) goes in unscaled.  Measured
-  // on MI355X over every 2^-23 grid value: radius error <= 4.7e-7, sine and cosine error
-  // <= 1.3e-7, so |error| <= 1.2e-6 for |x| < 5.65.
-  __device__ __forceinline__ void pair(uint32_t c, float *cs, float *sn) const {
-    const float u1 = unit23(word(hk, 2u * c));
-    const float u2 = unit23(word(hk, 2u * c + 1u));
-    const float r = __builtin_amdgcn_sqrtf(__builtin_amdgcn_logf(1.0f - u1) * -1.38629436111989061883f);
-    const float t = u2 >= 0.5f ? u2 - 1.0f : u2;  // a whole turn: angle in [-pi, pi)
-    *cs = r * __builtin_amdgcn_cosf(t);
-    *sn = r * __builtin_amdgcn_sinf(t);
-  }
+  // Pair c is the public API's tk_randn2_f32: r = sqrt(-2 ln(1 - u1)) with the hardware
+  // base-2 logarithm (ln x = ln 2 * log2 x) and square root; cos and sin of 2 pi t with the
+  // hardware sine and cosine, which take their argument in turns, so the wrapped t in
+  // [-1/2, 1/2) goes in unscaled.  Measured on MI355X over every 2^-23 grid value: radius
+  // error <= 4.7e-7, sine and cosine error <= 1.3e-7, so |error| <= 1.2e-6 for |x| < 5.65.
+  __device__ __forceinline__ void pair(uint32_t c, float *cs, float *sn) const { tk_randn2_f32(hk, c, cs, sn); }
   __device__ __forceinline__ float elem(uint64_t k) const {
     const uint64_t i = start + k;
     float c, s;
@@ -344,7 +337,7 @@ struct OpDropout : FillBase<float> {
   bool x_vec;      // x is 16-byte aligned where y is
   bool mask_word;  // mask is 4-byte aligned where y is 16-byte aligned
   __device__ __forceinline__ float elem(uint64_t k) const {
-    const bool keep = unit23(word(hk, (uint32_t)(start + k))) >= p;
+    const bool keep = tk_dropout_keep(p, hk, (uint32_t)(start + k));
     if (mask) mask[k] = (uint8_t)keep;
     return keep ? __fdiv_rn(x[k], q) : 0.0f;
   }
@@ -363,7 +356,7 @@ struct OpDropout : FillBase<float> {
     uint32_t y[4], m = 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const bool keep = unit23(word(hk, c + j)) >= p;
+      const bool keep = tk_dropout_keep(p, hk, c + j);
       y[j] = keep ? __float_as_uint(__fdiv_rn(xv[j], q)) : 0u;
       m |= (uint32_t)keep << (8 * j);
     }
@@ -642,6 +635,11 @@ tk_status tk_dropout_f32(uint32_t key, uint64_t start_draw, uint64_t n, float p,
   op.x_vec = (((uintptr_t)(x + op.head)) & 15u) == 0;
   op.mask_word = mask && (((uintptr_t)(mask + op.head)) & 3u) == 0;
   return launch_vec(op, stream);
+}
+
+tk_status tk_dropout_backward_f32(uint32_t key, uint64_t start_draw, uint64_t n, float p, const float *dy,
+                                  float *dx, hipStream_t stream) {
+  return tk_dropout_f32(key, start_draw, n, p, dy, dx, nullptr, stream);
 }
 
 tk_status tk_philox_fill_u32(uint64_t key, uint64_t start_draw, uint64_t n, uint32_t *out, hipStream_t stream) {

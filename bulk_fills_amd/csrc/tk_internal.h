@@ -7,6 +7,7 @@
 #include <mutex>
 
 #include "tk.h"
+#include "tk_device_api.h"
 
 namespace tk {
 
@@ -23,15 +24,8 @@ inline tk_status hip_status(hipError_t e) {
 // Status of the most recent kernel launch on this thread.
 inline tk_status launch_status() { return hip_status(hipGetLastError()); }
 
-// Host copy of the generator (the kernels use the __device__ one in tk_device.h).
-inline uint32_t host_lowbias32(uint32_t x) {
-  x ^= x >> 16;
-  x *= 0x7FEB352Du;
-  x ^= x >> 15;
-  x *= 0x846CA68Bu;
-  x ^= x >> 16;
-  return x;
-}
+// The generator's hash on the host (the public API's tk_hash32, shared with the kernels).
+inline uint32_t host_lowbias32(uint32_t x) { return tk_hash32(x); }
 
 // Purpose tags of sub(key, P) (ASCII "NORM", "BL32", "BL64").
 constexpr uint32_t kPurposeNormal64 = 0x4E4F524Du;

@@ -108,9 +108,9 @@ tk_status tk_fill_normal_f32(uint32_t key, uint64_t start_draw, uint64_t n, floa
  * tandem-sycl, "Design", §Exponentials; tandem-cuda, "Performance", §GPU (the f32
  * exponential maps 1 - exp(-x) back to the draw's own 2^-24 grid point).  x = -ln(1 - u),
  * +0.0 at u = 0, by inversion of the draw's uniform:
- *   f64: u = (u64 draw & (2^53 - 1)) 2^-53; x from the device f64 logarithm (within
- *        1 ulp of the exact value).                                      (i < 2^31)
- *   f32: u = (word i & 0xFFFFFF) 2^-24; x correctly rounded to f32 (evaluated in f64 and
+ *   f64: u = (u64 draw & (2^53 - 1)) 2^-53; x from the library's table-driven f64
+ *        logarithm (within 0.52 ulp of the exact value).                (i < 2^31)
+ *   f32: u = (word i & 0xFFFFFF) 2^-24; x correctly rounded to f32 (the same logarithm
  *        rounded once, which is exact at every one of the 2^24 grid points).  (i < 2^32) */
 tk_status tk_fill_exponential_f64(uint32_t key, uint64_t start_draw, uint64_t n, double *out, hipStream_t stream);
 tk_status tk_fill_exponential_f32(uint32_t key, uint64_t start_draw, uint64_t n, float *out, hipStream_t stream);
@@ -123,6 +123,15 @@ tk_status tk_fill_exponential_f32(uint32_t key, uint64_t start_draw, uint64_t n,
  * kept.  i < 2^32.                                                                       */
 tk_status tk_dropout_f32(uint32_t key, uint64_t start_draw, uint64_t n, float p, const float *x,
                          float *y, uint8_t *mask, hipStream_t stream);
+
+/* Dropout backward by redrawing (Phobos, §Random numbers: the same seed and counter give
+ * the same number, so a backward pass redraws its forward pass's mask instead of storing
+ * it): dx[k] = keep(k) ? dy[k] / (1 - p) : +0.0, where keep(k) is the decision of
+ * tk_dropout_f32 for the same key, start_draw + k and p.  The same computation as the
+ * forward call applied to dy with no mask output; same checks (dy and dx may be the same
+ * buffer, no other overlap).  i < 2^32.                                                 */
+tk_status tk_dropout_backward_f32(uint32_t key, uint64_t start_draw, uint64_t n, float p, const float *dy,
+                                  float *dx, hipStream_t stream);
 
 /* ---- Weighted choice through an alias table -----------------------------------------
  * tandem-sycl, "Design", §Fills: the choice fill maps each 64-bit draw through an alias

@@ -82,6 +82,12 @@ def test_dropout_validation():
     assert L.tk_dropout_f32(1, 0, 8, 0.1, FAKE, FAKE + 4, None, None) == tk.TK_EINVAL   # partial overlap
     assert L.tk_dropout_f32(1, U32MAX, 2, 0.1, FAKE, FAKE + 64, None, None) == tk.TK_ERANGE
     assert L.tk_dropout_f32(1, 0, 0, 0.1, None, None, None, None) == tk.TK_OK
+    for p in (-0.1, 1.0, float("nan")):
+        assert L.tk_dropout_backward_f32(1, 0, 4, p, FAKE, FAKE + 64, None) == tk.TK_EINVAL
+    assert L.tk_dropout_backward_f32(1, 0, 4, 0.1, None, FAKE, None) == tk.TK_EINVAL
+    assert L.tk_dropout_backward_f32(1, 0, 8, 0.1, FAKE, FAKE + 4, None) == tk.TK_EINVAL
+    assert L.tk_dropout_backward_f32(1, U32MAX, 2, 0.1, FAKE, FAKE + 64, None) == tk.TK_ERANGE
+    assert L.tk_dropout_backward_f32(1, 0, 0, 0.1, None, None, None) == tk.TK_OK
 
 
 def test_choice_and_alias_validation():
