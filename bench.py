@@ -107,8 +107,11 @@ def measured_traffic(fill):
     if not rec:
         return None
     h = hashlib.sha256()
-    for f in rec["sources"]:
-        h.update(open(os.path.join(here, "bulk_fills_amd", "csrc", f), "rb").read())
+    for f in rec["sources"]:  # paths relative to the repository root
+        path = os.path.join(here, f)
+        if not os.path.exists(path):
+            return None
+        h.update(open(path, "rb").read())
     return rec["traffic_bytes"] if h.hexdigest() == rec["source_sha256"] else None
 
 
