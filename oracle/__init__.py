@@ -114,6 +114,9 @@ philox_fill_u32 = _simple("orc_philox_fill_u32", np.uint32, _u32p, C.c_uint64)
 philox_fill_u64 = _simple("orc_philox_fill_u64", np.uint64, _u64p, C.c_uint64)
 philox_fill_f32 = _simple("orc_philox_fill_f32", np.float32, _fp, C.c_uint64)
 philox_fill_f64 = _simple("orc_philox_fill_f64", np.float64, _dp, C.c_uint64)
+philox_fill_normal_f32 = _simple("orc_philox_fill_normal_f32", np.float32, _fp, C.c_uint64)
+fill_normal_f32_half_turn = _simple("orc_fill_normal_f32_half_turn", np.float32, _fp)
+fill_randn_f32 = _simple("orc_fill_randn_f32", np.float32, _fp)
 
 _lib.orc_fill_u32_below.argtypes = [C.c_uint32, C.c_uint64, C.c_uint64, _u64p, C.c_uint32, _u32p]
 _lib.orc_fill_u64_below.argtypes = [C.c_uint32, C.c_uint64, C.c_uint64, _u64p, C.c_uint64, _u64p]
@@ -125,6 +128,13 @@ _lib.orc_dropout_f32.argtypes = [C.c_uint32, C.c_uint64, C.c_uint64, _u64p, C.c_
 _lib.orc_alias_build.argtypes = [_dp, C.c_uint32, _u32p, _u32p, _u64p]
 _lib.orc_fill_choice_u32.argtypes = [C.c_uint32, C.c_uint64, C.c_uint64, _u64p, _u32p, _u32p, C.c_uint32, _u32p]
 _lib.orc_zig_table.argtypes = [C.c_uint32, _dp, _dp, _dp, _dp]
+_lib.orc_philox_sub_word.restype = C.c_uint32
+_lib.orc_philox_sub_word.argtypes = [C.c_uint64, C.c_uint64, C.c_uint32, C.c_uint32]
+philox_sub_word = _lib.orc_philox_sub_word
+_lib.orc_philox_fill_u32_below.argtypes = [C.c_uint64, C.c_uint64, C.c_uint64, _u64p, C.c_uint32, _u32p]
+_lib.orc_philox_fill_u64_below.argtypes = [C.c_uint64, C.c_uint64, C.c_uint64, _u64p, C.c_uint64, _u64p]
+_lib.orc_philox_fill_choice_u32.argtypes = [C.c_uint64, C.c_uint64, C.c_uint64, _u64p, _u32p, _u32p, C.c_uint32, _u32p]
+_lib.orc_philox_fill_normal_f64.argtypes = [C.c_uint64, C.c_uint64, C.c_uint64, _u64p, _dp, _u8p]
 
 
 def _n(n, d):
@@ -207,6 +217,40 @@ def fill_choice_u32(key, start, n, q, alias, draws=None):
     _check(_lib.orc_fill_choice_u32(key, start, out.size, dp, _ptr(q, _u32p), _ptr(alias, _u32p), q.size,
                                     _ptr(out, _u32p)), "choice_u32")
     return out
+
+
+def philox_fill_u32_below(key, start=0, n=None, bound=1, draws=None):
+    d, dp = _draws(draws)
+    out = np.empty(_n(n, d), dtype=np.uint32)
+    _check(_lib.orc_philox_fill_u32_below(key, start, out.size, dp, bound, _ptr(out, _u32p)), "philox_u32_below")
+    return out
+
+
+def philox_fill_u64_below(key, start=0, n=None, bound=1, draws=None):
+    d, dp = _draws(draws)
+    out = np.empty(_n(n, d), dtype=np.uint64)
+    _check(_lib.orc_philox_fill_u64_below(key, start, out.size, dp, bound, _ptr(out, _u64p)), "philox_u64_below")
+    return out
+
+
+def philox_fill_choice_u32(key, start, n, q, alias, draws=None):
+    q = np.ascontiguousarray(q, dtype=np.uint32)
+    alias = np.ascontiguousarray(alias, dtype=np.uint32)
+    d, dp = _draws(draws)
+    out = np.empty(_n(n, d), dtype=np.uint32)
+    _check(_lib.orc_philox_fill_choice_u32(key, start, out.size, dp, _ptr(q, _u32p), _ptr(alias, _u32p), q.size,
+                                           _ptr(out, _u32p)), "philox_choice_u32")
+    return out
+
+
+def philox_fill_normal_f64(key, start=0, n=None, draws=None, with_path=False):
+    """As fill_normal_f64 over the Philox source."""
+    d, dp = _draws(draws)
+    out = np.empty(_n(n, d), dtype=np.float64)
+    path = np.empty(out.size, dtype=np.uint8) if with_path else None
+    _check(_lib.orc_philox_fill_normal_f64(key, start, out.size, dp, _ptr(out, _dp), _ptr(path, _u8p)),
+           "philox_normal_f64")
+    return (out, path) if with_path else out
 
 
 _lib.orc_lemire32_map.argtypes = [_u32p, C.c_uint64, C.c_uint32, _u32p, _u8p]

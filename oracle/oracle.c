@@ -76,6 +76,68 @@ static uint64_t draw64(uint32_t key, uint32_t i)
 }
 
 /* ---------------------------------------------------------------------------------
+ * Draw sources.  Bounded draws, the ziggurat and Box-Muller are defined once over a
+ * source: the lowbias32 stream of a 32-bit key, or Philox4x32-10 (defined further down)
+ * of a 64-bit key.  A source gives word i, the 64-bit draw i (words 2i low, 2i+1 high)
+ * and, for a purpose P, the substream of draw i:
+ *   lowbias32: substream word j of draw i is word(split(sub(key, P), i), j) (above);
+ *   Philox, READING: substream word j of draw i is lane j & 3 of the Philox block of the
+ *     same key with counter (lo32 i, hi32 i, P, j >> 2).  The primary stream's blocks
+ *     have counter words 2 and 3 zero, so P != 0 keeps the two disjoint.
+ * A 64-bit substream draw j is substream words 2j (low) and 2j+1 (high).
+ * ------------------------------------------------------------------------------- */
+typedef struct {
+    int philox;
+    uint32_t key32;
+    uint64_t key64;
+} src_t;
+
+static void philox_block(uint64_t key, const uint32_t ctr[4], uint32_t out[4]);
+
+static src_t lowbias_src(uint32_t key)
+{
+    src_t s = {0, key, 0};
+    return s;
+}
+
+static src_t philox_src(uint64_t key)
+{
+    src_t s = {1, 0, key};
+    return s;
+}
+
+static uint32_t philox_ctr_word(uint64_t key, uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
+                                uint32_t lane)
+{
+    uint32_t ctr[4] = {c0, c1, c2, c3}, out[4];
+    philox_block(key, ctr, out);
+    return out[lane];
+}
+
+static uint32_t src_word(const src_t *s, uint64_t i)
+{
+    if (!s->philox) return orc_word(s->key32, (uint32_t)i);
+    uint64_t b = i >> 2;
+    return philox_ctr_word(s->key64, (uint32_t)b, (uint32_t)(b >> 32), 0u, 0u, (uint32_t)(i & 3u));
+}
+
+static uint64_t src_draw64(const src_t *s, uint64_t i)
+{
+    return (uint64_t)src_word(s, 2u * i) | ((uint64_t)src_word(s, 2u * i + 1u) << 32);
+}
+
+static uint32_t src_sub_word(const src_t *s, uint32_t purpose, uint64_t i, uint32_t j)
+{
+    if (!s->philox) return orc_word(orc_split(orc_sub(s->key32, purpose), (uint32_t)i), j);
+    return philox_ctr_word(s->key64, (uint32_t)i, (uint32_t)(i >> 32), purpose, j >> 2, j & 3u);
+}
+
+static uint64_t src_sub_draw64(const src_t *s, uint32_t purpose, uint64_t i, uint32_t j)
+{
+    return (uint64_t)src_sub_word(s, purpose, i, 2u * j) | ((uint64_t)src_sub_word(s, purpose, i, 2u * j + 1u) << 32);
+}
+
+/* ---------------------------------------------------------------------------------
  * Draw-index checks.  Counters are 32-bit (the Phobos hash takes an i32); a fill whose
  * draws would need a counter at or beyond 2^32 is refused rather than wrapped.
  * READING.
@@ -218,24 +280,34 @@ static int lemire64_step(uint64_t x, uint64_t s, uint64_t t, uint64_t *r)
     return (uint64_t)m >= t;
 }
 
-uint32_t orc_lemire32(uint32_t key, uint32_t i, uint32_t s)
+static uint32_t lemire32_src(const src_t *src, uint64_t i, uint32_t s)
 {
     uint32_t t = (uint32_t)(0u - s) % s, r;
-    if (lemire32_step(orc_word(key, i), s, t, &r)) return r;
-    uint32_t sg = orc_split(orc_sub(key, ORC_P_BELOW32), i);
+    if (lemire32_step(src_word(src, i), s, t, &r)) return r;
     for (uint32_t j = 0; j < SUBSTREAM_CAP; ++j)
-        if (lemire32_step(orc_word(sg, j), s, t, &r)) break;
+        if (lemire32_step(src_sub_word(src, ORC_P_BELOW32, i, j), s, t, &r)) break;
     return r;
+}
+
+static uint64_t lemire64_src(const src_t *src, uint64_t i, uint64_t s)
+{
+    uint64_t t = (0ull - s) % s, r;
+    if (lemire64_step(src_draw64(src, i), s, t, &r)) return r;
+    for (uint32_t j = 0; j < SUBSTREAM_CAP; ++j)
+        if (lemire64_step(src_sub_draw64(src, ORC_P_BELOW64, i, j), s, t, &r)) break;
+    return r;
+}
+
+uint32_t orc_lemire32(uint32_t key, uint32_t i, uint32_t s)
+{
+    src_t src = lowbias_src(key);
+    return lemire32_src(&src, i, s);
 }
 
 uint64_t orc_lemire64(uint32_t key, uint32_t i, uint64_t s)
 {
-    uint64_t t = (0ull - s) % s, r;
-    if (lemire64_step(draw64(key, i), s, t, &r)) return r;
-    uint32_t sg = orc_split(orc_sub(key, ORC_P_BELOW64), i);
-    for (uint32_t j = 0; j < SUBSTREAM_CAP; ++j)
-        if (lemire64_step(draw64(sg, j), s, t, &r)) break;
-    return r;
+    src_t src = lowbias_src(key);
+    return lemire64_src(&src, i, s);
 }
 
 /* The multiply-shift step alone over given words (no hashing, no retry), so a test can
@@ -336,10 +408,9 @@ static void zig_init(void)
 
 static double unit53(uint64_t d) { return (double)(d >> 11) * 0x1p-53; }
 
-static double zig_normal(uint32_t key, uint32_t i, uint8_t *path)
+static double zig_normal(const src_t *src, uint64_t i, uint8_t *path)
 {
-    uint64_t d = draw64(key, i);
-    uint32_t sg = orc_split(orc_sub(key, ORC_P_NORMAL64), i);
+    uint64_t d = src_draw64(src, i);
     uint32_t j = 0; /* next substream position (64-bit draws) */
     int restarted = 0;
     for (;;) {
@@ -353,8 +424,8 @@ static double zig_normal(uint32_t key, uint32_t i, uint8_t *path)
         if (L == 0) {
             for (;;) {
                 if (j + 2 > SUBSTREAM_CAP) return NAN;
-                uint64_t a = draw64(sg, j++);
-                uint64_t b = draw64(sg, j++);
+                uint64_t a = src_sub_draw64(src, ORC_P_NORMAL64, i, j++);
+                uint64_t b = src_sub_draw64(src, ORC_P_NORMAL64, i, j++);
                 double ua = (double)((a >> 11) + 1u) * 0x1p-53;
                 double ub = (double)((b >> 11) + 1u) * 0x1p-53;
                 double xi = -log(ua) / zig_r;
@@ -367,14 +438,14 @@ static double zig_normal(uint32_t key, uint32_t i, uint8_t *path)
             }
         }
         if (j + 1 > SUBSTREAM_CAP) return NAN;
-        double y = unit53(draw64(sg, j++));
+        double y = unit53(src_sub_draw64(src, ORC_P_NORMAL64, i, j++));
         double fy = zig_f[L] + y * (zig_f[L + 1] - zig_f[L]);
         if (fy < exp(-0.5 * (x * x))) {
             if (path) *path = 1;
             return neg ? -x : x;
         }
         if (j + 1 > SUBSTREAM_CAP) return NAN;
-        d = draw64(sg, j++);
+        d = src_sub_draw64(src, ORC_P_NORMAL64, i, j++);
         restarted = 1;
     }
 }
@@ -384,8 +455,9 @@ int orc_fill_normal_f64(uint32_t key, uint64_t start, uint64_t n, const uint64_t
 {
     CHECK(MAX_DRAW_W64);
     zig_init();
+    src_t src = lowbias_src(key);
     for (uint64_t k = 0; k < n; ++k)
-        out[k] = zig_normal(key, (uint32_t)DRAW(k), path ? path + k : NULL);
+        out[k] = zig_normal(&src, DRAW(k), path ? path + k : NULL);
     return ORC_OK;
 }
 
@@ -398,13 +470,17 @@ int orc_fill_normal_f64(uint32_t key, uint64_t start, uint64_t n, const uint64_t
  * equals Phobos randn's cos(2 pi u2)).  Evaluated in f64 from the exact f32 uniforms and
  * rounded once to f32.
  * ------------------------------------------------------------------------------- */
-static float box_muller(uint32_t key, uint64_t i)
+static float unit23_of(uint32_t w) { return (float)(w & 8388607u) * 1.1920928955078125e-7f; }
+
+static float box_muller(const src_t *src, uint64_t i, int half_turn)
 {
-    uint32_t c = (uint32_t)(i >> 1);
-    float u1 = orc_uniform(key, 2u * c);
-    float u2 = orc_uniform(key, 2u * c + 1u);
+    uint64_t c = i >> 1;
+    float u1 = unit23_of(src_word(src, 2u * c));
+    float u2 = unit23_of(src_word(src, 2u * c + 1u));
     double r = sqrt(-2.0 * log(1.0 - (double)u1));
-    double t = u2 >= 0.5f ? (double)u2 - 1.0 : (double)u2;
+    double t;
+    if (half_turn) t = (double)u2 - 0.5;
+    else t = u2 >= 0.5f ? (double)u2 - 1.0 : (double)u2;
     double theta = 6.283185307179586 * t;
     return (float)((i & 1u) ? r * sin(theta) : r * cos(theta));
 }
@@ -412,7 +488,28 @@ static float box_muller(uint32_t key, uint64_t i)
 int orc_fill_normal_f32(uint32_t key, uint64_t start, uint64_t n, const uint64_t *draws, float *out)
 {
     CHECK(MAX_DRAW_W32);
-    for (uint64_t k = 0; k < n; ++k) out[k] = box_muller(key, DRAW(k));
+    src_t src = lowbias_src(key);
+    for (uint64_t k = 0; k < n; ++k) out[k] = box_muller(&src, DRAW(k), 0);
+    return ORC_OK;
+}
+
+/* tandem-sycl, "Design", §Normals: the float normal fill shifts the angle by half a turn
+ * into [-pi, pi).  READING: t = u2 - 1/2, so theta = 2 pi u2 - pi and both values are the
+ * negation of the whole-turn fill's (cos and sin of theta - pi); same pairs and radius. */
+int orc_fill_normal_f32_half_turn(uint32_t key, uint64_t start, uint64_t n, const uint64_t *draws, float *out)
+{
+    CHECK(MAX_DRAW_W32);
+    src_t src = lowbias_src(key);
+    for (uint64_t k = 0; k < n; ++k) out[k] = box_muller(&src, DRAW(k), 1);
+    return ORC_OK;
+}
+
+/* Phobos, §randn: one normal per counter, randn(key, c) for c = start + k, exactly as the
+ * page prints it (orc_randn).  Counters c < 2^31 (words 2c and 2c+1). */
+int orc_fill_randn_f32(uint32_t key, uint64_t start, uint64_t n, const uint64_t *draws, float *out)
+{
+    CHECK(0x7FFFFFFFull);
+    for (uint64_t k = 0; k < n; ++k) out[k] = orc_randn(key, (uint32_t)DRAW(k));
     return ORC_OK;
 }
 
@@ -567,10 +664,9 @@ int orc_fill_choice_u32(uint32_t key, uint64_t start, uint64_t n, const uint64_t
  * lo(lane0 product)); the key is bumped by 0x9E3779B9 and 0xBB67AE85 between rounds.
  * Parity unpinned: no known-answer vectors are available here.
  * ------------------------------------------------------------------------------- */
-static uint32_t philox_word(uint64_t key, uint64_t w)
+static void philox_block(uint64_t key, const uint32_t ctr[4], uint32_t out[4])
 {
-    uint64_t b = w >> 2;
-    uint32_t c[4] = {(uint32_t)b, (uint32_t)(b >> 32), 0u, 0u};
+    uint32_t c[4] = {ctr[0], ctr[1], ctr[2], ctr[3]};
     uint32_t k0 = (uint32_t)key, k1 = (uint32_t)(key >> 32);
     for (int round = 0; round < 10; ++round) {
         if (round) {
@@ -585,7 +681,13 @@ static uint32_t philox_word(uint64_t key, uint64_t w)
         uint32_t n3 = (uint32_t)p0;
         c[0] = n0; c[1] = n1; c[2] = n2; c[3] = n3;
     }
-    return c[w & 3u];
+    for (int j = 0; j < 4; ++j) out[j] = c[j];
+}
+
+static uint32_t philox_word(uint64_t key, uint64_t w)
+{
+    uint64_t b = w >> 2;
+    return philox_ctr_word(key, (uint32_t)b, (uint32_t)(b >> 32), 0u, 0u, (uint32_t)(w & 3u));
 }
 
 #define MAX_DRAW_PHILOX_W32 0xFFFFFFFFFFFFFFFFull
@@ -623,5 +725,71 @@ int orc_philox_fill_f64(uint64_t key, uint64_t start, uint64_t n, const uint64_t
     CHECK(MAX_DRAW_PHILOX_W64);
     for (uint64_t k = 0; k < n; ++k)
         out[k] = (double)(philox_draw64(key, DRAW(k)) & ((1ull << 53) - 1u)) * 0x1p-53;
+    return ORC_OK;
+}
+
+/* ---------------------------------------------------------------------------------
+ * Philox variants of the bounded, choice and normal fills: the same definitions as the
+ * lowbias32 fills above over the Philox source (src_t): word i, 64-bit draw i, and the
+ * per-draw substreams with counter (lo32 i, hi32 i, P, j >> 2).  Parity unpinned (the
+ * Philox word source has no known-answer vectors here).
+ * ------------------------------------------------------------------------------- */
+/* Substream word j of draw i for purpose P (exposed for the tests). */
+uint32_t orc_philox_sub_word(uint64_t key, uint64_t i, uint32_t purpose, uint32_t j)
+{
+    src_t src = philox_src(key);
+    return src_sub_word(&src, purpose, i, j);
+}
+
+int orc_philox_fill_u32_below(uint64_t key, uint64_t start, uint64_t n, const uint64_t *draws,
+                              uint32_t bound, uint32_t *out)
+{
+    if (bound == 0) return ORC_EINVAL;
+    CHECK(MAX_DRAW_PHILOX_W32);
+    src_t src = philox_src(key);
+    for (uint64_t k = 0; k < n; ++k) out[k] = lemire32_src(&src, DRAW(k), bound);
+    return ORC_OK;
+}
+
+int orc_philox_fill_u64_below(uint64_t key, uint64_t start, uint64_t n, const uint64_t *draws,
+                              uint64_t bound, uint64_t *out)
+{
+    if (bound == 0) return ORC_EINVAL;
+    CHECK(MAX_DRAW_PHILOX_W64);
+    src_t src = philox_src(key);
+    for (uint64_t k = 0; k < n; ++k) out[k] = lemire64_src(&src, DRAW(k), bound);
+    return ORC_OK;
+}
+
+int orc_philox_fill_choice_u32(uint64_t key, uint64_t start, uint64_t n, const uint64_t *draws,
+                               const uint32_t *q, const uint32_t *alias, uint32_t ncat, uint32_t *out)
+{
+    if (ncat == 0 || !q || !alias) return ORC_EINVAL;
+    CHECK(MAX_DRAW_PHILOX_W64);
+    src_t src = philox_src(key);
+    for (uint64_t k = 0; k < n; ++k) {
+        uint64_t d = src_draw64(&src, DRAW(k));
+        uint32_t column = (uint32_t)(((d >> 32) * (uint64_t)ncat) >> 32);
+        uint32_t coin = (uint32_t)d;
+        out[k] = coin < q[column] ? column : alias[column];
+    }
+    return ORC_OK;
+}
+
+int orc_philox_fill_normal_f32(uint64_t key, uint64_t start, uint64_t n, const uint64_t *draws, float *out)
+{
+    CHECK(MAX_DRAW_PHILOX_W32);
+    src_t src = philox_src(key);
+    for (uint64_t k = 0; k < n; ++k) out[k] = box_muller(&src, DRAW(k), 0);
+    return ORC_OK;
+}
+
+int orc_philox_fill_normal_f64(uint64_t key, uint64_t start, uint64_t n, const uint64_t *draws,
+                               double *out, uint8_t *path)
+{
+    CHECK(MAX_DRAW_PHILOX_W64);
+    zig_init();
+    src_t src = philox_src(key);
+    for (uint64_t k = 0; k < n; ++k) out[k] = zig_normal(&src, DRAW(k), path ? path + k : NULL);
     return ORC_OK;
 }

@@ -25,8 +25,9 @@
  * Tsang (2000) for the ziggurat construction, Lemire (2019) for the exact rejection
  * threshold, Vose (1991) for the alias table, Salmon et al. (SC'11) for Philox4x32-10.
  *
- * Parity unpinned: orc_philox_* (no known-answer vectors are available to check it
- * against; only the shared definition and statistics tie it down).
+ * Parity unpinned: orc_philox_* (no known-answer vectors are available to check the
+ * Philox word source against; only the shared definition and statistics tie it down,
+ * and the Philox bounded, choice and normal variants reduce to pinned maps over it).
  */
 #ifndef BULK_FILLS_ORACLE_H
 #define BULK_FILLS_ORACLE_H
@@ -84,6 +85,12 @@ int orc_fill_normal_f64(uint32_t key, uint64_t start, uint64_t n, const uint64_t
                         double *out, uint8_t *path);
 int orc_fill_normal_f32(uint32_t key, uint64_t start, uint64_t n, const uint64_t *draws,
                         float *out);
+/* The pages' half-turn Box-Muller (angle 2 pi u2 - pi): the negation of the above. */
+int orc_fill_normal_f32_half_turn(uint32_t key, uint64_t start, uint64_t n, const uint64_t *draws,
+                                  float *out);
+/* Phobos randn, one normal per counter: element k = randn(key, start + k). */
+int orc_fill_randn_f32(uint32_t key, uint64_t start, uint64_t n, const uint64_t *draws,
+                       float *out);
 
 /* Exponentials: x = -ln(1 - u); f64 from the f64 uniform, f32 from a 2^-24 grid (rounded
  * once from f64). */
@@ -116,6 +123,21 @@ int orc_philox_fill_f32(uint64_t key, uint64_t start, uint64_t n, const uint64_t
                         float *out);
 int orc_philox_fill_f64(uint64_t key, uint64_t start, uint64_t n, const uint64_t *draws,
                         double *out);
+
+/* Philox variants of the bounded, choice and normal fills (same definitions over the
+ * Philox source; a rejected or missed draw i continues on Philox blocks with counter
+ * (lo32 i, hi32 i, purpose, j >> 2)). */
+uint32_t orc_philox_sub_word(uint64_t key, uint64_t i, uint32_t purpose, uint32_t j);
+int orc_philox_fill_u32_below(uint64_t key, uint64_t start, uint64_t n, const uint64_t *draws,
+                              uint32_t bound, uint32_t *out);
+int orc_philox_fill_u64_below(uint64_t key, uint64_t start, uint64_t n, const uint64_t *draws,
+                              uint64_t bound, uint64_t *out);
+int orc_philox_fill_choice_u32(uint64_t key, uint64_t start, uint64_t n, const uint64_t *draws,
+                               const uint32_t *q, const uint32_t *alias, uint32_t ncat, uint32_t *out);
+int orc_philox_fill_normal_f32(uint64_t key, uint64_t start, uint64_t n, const uint64_t *draws,
+                               float *out);
+int orc_philox_fill_normal_f64(uint64_t key, uint64_t start, uint64_t n, const uint64_t *draws,
+                               double *out, uint8_t *path);
 
 #ifdef __cplusplus
 }

@@ -204,6 +204,12 @@ FILLS = {
     "i64_below": lambda k, s, n, draws=None: oracle.fill_i64_below(k, s, n, -(1 << 40), 1 << 41, draws=draws),
     "philox_u32": oracle.philox_fill_u32, "philox_f64": oracle.philox_fill_f64,
     "exponential_f64": oracle.fill_exponential_f64, "exponential_f32": oracle.fill_exponential_f32,
+    "normal_f32_half_turn": oracle.fill_normal_f32_half_turn, "randn_f32": oracle.fill_randn_f32,
+    "philox_u32_below": lambda k, s, n, draws=None: oracle.philox_fill_u32_below(k, s, n, (1 << 31) + 1, draws=draws),
+    "philox_u64_below": lambda k, s, n, draws=None: oracle.philox_fill_u64_below(k, s, n, (1 << 63) + 1, draws=draws),
+    "philox_normal_f32": oracle.philox_fill_normal_f32, "philox_normal_f64": oracle.philox_fill_normal_f64,
+    "philox_choice": lambda k, s, n, draws=None: oracle.philox_fill_choice_u32(
+        k, s, n, *oracle.alias_build([1.0, 2.0, 3.0])[:2], draws=draws),
 }
 
 
@@ -673,3 +679,142 @@ def test_exponential_f64_accuracy_and_law():
     assert stats.kstest(z[: 1 << 20], "expon").pvalue > 1e-4
     f = oracle.fill_exponential_f32(1, 0, 0, draws=rng.integers(0, 1 << 32, n, dtype=np.uint64))
     assert abs(f.mean() - 1) < 5 / math.sqrt(n) and f.min() >= 0
+
+
+# ---------------------------------------------------------------------------------------
+# Generator and normal variants: Philox sources for the bounded, choice and normal fills;
+# the pages' half-turn Box-Muller (tandem-sycl "Design" §Normals); Phobos's one normal per
+# counter (§randn).  The Philox word source stays parity unpinned; these pins tie each
+# variant to the maps and laws pinned above.
+# ---------------------------------------------------------------------------------------
+PK = 0x0123456789ABCDEF
+
+
+def test_philox_substream_layout():
+    """Substream word j of draw i is lane j & 3 of the block with counter
+    (lo32 i, hi32 i, P, j >> 2): with P = 0 and j < 4 that is the primary block i."""
+    for i in (0, 1, 5, (1 << 32) + 3, (1 << 40) + 17):
+        prim = oracle.philox_fill_u32(PK, 4 * i, 4)
+        assert [oracle.philox_sub_word(PK, i, 0, j) for j in range(4)] == list(prim)
+    a = [oracle.philox_sub_word(PK, 9, oracle.P_BELOW32, j) for j in range(8)]
+    b = [oracle.philox_sub_word(PK, 9, oracle.P_BELOW64, j) for j in range(8)]
+    c = [oracle.philox_sub_word(PK, 10, oracle.P_BELOW32, j) for j in range(8)]
+    assert len({tuple(a), tuple(b), tuple(c)}) == 3
+    assert not set(a) & set(oracle.philox_fill_u32(PK, 0, 64))
+
+
+@pytest.mark.parametrize("s", [1000, (1 << 31) + 1])
+def test_philox_bounded_is_map_then_substream(s):
+    start, n = (1 << 33) + 5, 4096
+    out = oracle.philox_fill_u32_below(PK, start, n, s)
+    v, acc = oracle.lemire32_map(oracle.philox_fill_u32(PK, start, n), s)
+    assert np.array_equal(out[acc], v[acc])
+    for k in np.flatnonzero(~acc)[:200]:
+        for j in range(64):
+            w = oracle.philox_sub_word(PK, start + int(k), oracle.P_BELOW32, j)
+            vv, aa = oracle.lemire32_map(np.array([w], dtype=np.uint32), s)
+            if aa[0]:
+                break
+        assert out[k] == vv[0]
+    if s == (1 << 31) + 1:
+        assert 0.45 < (~acc).mean() < 0.55
+        # retried values are uniform too (a retry that reused the rejected word would not be)
+        r = out[~acc]
+        assert stats.chisquare(np.bincount((r.astype(np.uint64) * 16 // s).astype(np.int64), minlength=16))[1] > 1e-4
+
+
+def test_philox_bounded64_is_map_then_substream():
+    start, n, s = 77, 4096, (1 << 63) + 1
+    out = oracle.philox_fill_u64_below(PK, start, n, s)
+    v, acc = oracle.lemire64_map(oracle.philox_fill_u64(PK, start, n), s)
+    assert np.array_equal(out[acc], v[acc])
+    for k in np.flatnonzero(~acc)[:100]:
+        for j in range(64):
+            d = oracle.philox_sub_word(PK, start + int(k), oracle.P_BELOW64, 2 * j) | (
+                oracle.philox_sub_word(PK, start + int(k), oracle.P_BELOW64, 2 * j + 1) << 32)
+            vv, aa = oracle.lemire64_map(np.array([d], dtype=np.uint64), s)
+            if aa[0]:
+                break
+        assert out[k] == vv[0]
+    small = oracle.philox_fill_u64_below(PK, 0, 1 << 16, 1000)
+    assert small.max() < 1000 and stats.chisquare(np.bincount(small.astype(np.int64), minlength=1000))[1] > 1e-4
+
+
+def test_philox_choice_is_the_alias_map_of_philox_draws():
+    w = (np.arange(1000) + 1.0) ** -1.1
+    q, al, _ = oracle.alias_build(w)
+    d = oracle.philox_fill_u64(PK, 3, 4096)
+    col = ((d >> np.uint64(32)) * np.uint64(1000) >> np.uint64(32)).astype(np.int64)
+    coin = (d & np.uint64(M32)).astype(np.uint32)
+    assert np.array_equal(oracle.philox_fill_choice_u32(PK, 3, 4096, q, al), np.where(coin < q[col], col, al[col]))
+    N = 1 << 21
+    counts = np.bincount(oracle.philox_fill_choice_u32(PK, 0, N, q, al), minlength=1000)
+    assert stats.chisquare(counts, w / w.sum() * N)[1] > 1e-4
+
+
+def test_philox_box_muller_geometry_and_law():
+    n = 1 << 16
+    z = oracle.philox_fill_normal_f32(PK, 0, 2 * n).astype(np.float64)
+    u = oracle.philox_fill_f32(PK, 0, 2 * n).astype(np.float64)
+    u1, u2 = u[0::2], u[1::2]
+    r2 = -2.0 * np.log1p(-u1)
+    ok = r2 > 1e-4
+    assert np.max(np.abs((z[0::2] ** 2 + z[1::2] ** 2)[ok] / r2[ok] - 1)) < 1e-6
+    t = np.where(u2 >= 0.5, u2 - 1, u2)
+    d = np.angle(np.exp(1j * (np.arctan2(z[1::2], z[0::2]) - 2 * np.pi * t)))
+    assert np.max(np.abs(d[r2 > 1e-2])) < 1e-5
+    assert np.array_equal(oracle.philox_fill_normal_f32(PK, 1, 9), z[1:10].astype(np.float32))
+    big = oracle.philox_fill_normal_f32(PK, 1 << 40, 1 << 20).astype(np.float64)
+    assert stats.kstest(big, "norm").pvalue > 1e-4
+
+
+def test_philox_ziggurat_fast_path_and_law(zig1024):
+    """Draw by draw, the fast path of the Philox ziggurat is that of its Philox 64-bit
+    draws (layer, sign and threshold as pinned above), and the values follow the normal law."""
+    X, F, r, v = zig1024
+    N = 1024
+    n = 1 << 19
+    d = oracle.philox_fill_u64(PK, 0, n)
+    z, path = oracle.philox_fill_normal_f64(PK, 0, n, with_path=True)
+    L = (d & np.uint64(N - 1)).astype(np.int64)
+    x = (d >> np.uint64(11)).astype(np.float64) * 2.0 ** -53 * X[L]
+    fast = x < X[L + 1]
+    assert np.array_equal(path == 0, fast)
+    sign = ((d >> np.uint64(10)) & np.uint64(1)).astype(bool)
+    assert np.array_equal(z[fast], np.where(sign[fast], -x[fast], x[fast]))
+    assert abs((~fast).mean() - 0.0042765667) < 5 * math.sqrt(0.0043 / n)
+    big, bpath = oracle.philox_fill_normal_f64(PK, 1 << 40, 1 << 22, with_path=True)
+    assert (bpath == 1).any() and (bpath == 2).any()
+    edges = special.ndtri(np.linspace(0, 1, 1025)[1:-1])
+    assert stats.chisquare(np.bincount(np.searchsorted(edges, big), minlength=1024))[1] > 1e-4
+    assert np.abs(big[bpath == 2]).min() > r
+
+
+def test_half_turn_box_muller_negates_the_whole_turn():
+    """Angle 2 pi u2 - pi: the same pairs and radius with both values negated (to within
+    one f32 rounding, since the two angles round differently in f64; next to a zero of
+    cos or sin both values are ~1e-16 and need not be opposite)."""
+    n = 1 << 18
+    h = oracle.fill_normal_f32_half_turn(4, 0, n)
+    w = oracle.fill_normal_f32(4, 0, n)
+    diff = np.abs(h.astype(np.float64) + w.astype(np.float64))
+    assert np.all(diff <= np.maximum(np.spacing(np.abs(w)).astype(np.float64), 1e-12))
+    assert (diff == 0).mean() > 0.999
+    u = oracle.fill_f32(4, 0, n).astype(np.float64)
+    ang = np.arctan2(h[1::2].astype(np.float64), h[0::2].astype(np.float64))
+    dd = np.angle(np.exp(1j * (ang - (2 * np.pi * u[1::2] - np.pi))))
+    r2 = -2.0 * np.log1p(-u[0::2])
+    assert np.max(np.abs(dd[r2 > 1e-2])) < 1e-5
+
+
+def test_randn_fill_is_phobos_randn_per_counter():
+    """Element k is randn(key, start + k): the cosine of Box-Muller pair start + k, i.e. the
+    even element 2(start + k) of the pair fill, to within one f32 rounding."""
+    s, n = 11, 1 << 16
+    z = oracle.fill_randn_f32(3, s, n)
+    pairs = oracle.fill_normal_f32(3, 2 * s, 2 * n)
+    diff = np.abs(z.astype(np.float64) - pairs[0::2].astype(np.float64))
+    assert np.all(diff <= np.spacing(np.abs(pairs[0::2])).astype(np.float64))
+    assert np.array_equal(z[:64], np.array([oracle.randn(3, s + c) for c in range(64)], dtype=np.float32))
+    with pytest.raises(oracle.OracleError):
+        oracle.fill_randn_f32(3, (1 << 31) - 1, 2)
