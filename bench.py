@@ -83,6 +83,14 @@ def build_step(tk, torch, n):
         ("exponential_f32", 4 * n, 0, 1, lambda s: tk.tk_fill_exponential_f32(ks(s), st(s), n, optr)),
         ("dropout_backward_f32", 4 * n, 4 * n, 1,
          lambda s: tk.tk_dropout_backward_f32(ti.DROPOUT_KEY, 0, n, ti.DROPOUT_P, x.data_ptr(), optr)),
+        # generator and normal variants
+        ("philox_u32_below_1000", 4 * n, 0, 1, lambda s: tk.tk_philox_fill_u32_below(1, st(s), n, 1000, optr)),
+        ("philox_u64_below_1000", 8 * n, 0, 1, lambda s: tk.tk_philox_fill_u64_below(1, st(s), n, 1000, optr)),
+        ("philox_choice_u32", 4 * n, 0, 1, lambda s: tk.tk_philox_fill_choice_u32(1, 0, n, table, optr)),
+        ("philox_normal_f32", 4 * n, 0, 1, lambda s: tk.tk_philox_fill_normal_f32(1, st(s), n, optr)),
+        ("philox_normal_f64", 8 * n, 0, zig_kernels, lambda s: tk.tk_philox_fill_normal_f64(1, st(s), n, optr)),
+        ("normal_f32_half_turn", 4 * n, 0, 1, lambda s: tk.tk_fill_normal_f32_half_turn(1, st(s), n, optr)),
+        ("randn_f32", 4 * n, 0, 1, lambda s: tk.tk_fill_randn_f32(1, 0, n, optr)),
         # short fills (latency rows: 4 MiB and 8 MiB sit in the caches)
         ("u32_2^20", 4 * m20, 0, 1, lambda s: tk.tk_fill_u32(1, 0, m20, optr)),
         ("normal_f64_2^20", 8 * m20, 0, zig_kernels, lambda s: tk.tk_fill_normal_f64(1, st(s), m20, optr)),

@@ -54,6 +54,8 @@ SIGNATURES = {
     "tk_fill_i64_below": [_u32, _u64, _u64, _i64, _u64, _p, _p],
     "tk_fill_normal_f64": [_u32, _u64, _u64, _p, _p],
     "tk_fill_normal_f32": [_u32, _u64, _u64, _p, _p],
+    "tk_fill_normal_f32_half_turn": [_u32, _u64, _u64, _p, _p],
+    "tk_fill_randn_f32": [_u32, _u64, _u64, _p, _p],
     "tk_fill_exponential_f64": [_u32, _u64, _u64, _p, _p],
     "tk_fill_exponential_f32": [_u32, _u64, _u64, _p, _p],
     "tk_dropout_f32": [_u32, _u64, _u64, _f32, _p, _p, _p, _p],
@@ -67,6 +69,11 @@ SIGNATURES = {
     "tk_philox_fill_u64": [_u64, _u64, _u64, _p, _p],
     "tk_philox_fill_f32": [_u64, _u64, _u64, _p, _p],
     "tk_philox_fill_f64": [_u64, _u64, _u64, _p, _p],
+    "tk_philox_fill_u32_below": [_u64, _u64, _u64, _u32, _p, _p],
+    "tk_philox_fill_u64_below": [_u64, _u64, _u64, _u64, _p, _p],
+    "tk_philox_fill_choice_u32": [_u64, _u64, _u64, _p, _p, _p],
+    "tk_philox_fill_normal_f32": [_u64, _u64, _u64, _p, _p],
+    "tk_philox_fill_normal_f64": [_u64, _u64, _u64, _p, _p],
     "tk_ziggurat_table": [_p, _p],
     "tk_debug_set_miss_capacity": [_u32, _u64],
     "tk_debug_last_miss_count": [_p],
@@ -144,12 +151,26 @@ tk_fill_f64 = _fill("tk_fill_f64", 8)
 tk_fill_bool = _fill("tk_fill_bool", 1)
 tk_fill_normal_f64 = _fill("tk_fill_normal_f64", 8)
 tk_fill_normal_f32 = _fill("tk_fill_normal_f32", 4)
+tk_fill_normal_f32_half_turn = _fill("tk_fill_normal_f32_half_turn", 4)
+tk_fill_randn_f32 = _fill("tk_fill_randn_f32", 4)
 tk_fill_exponential_f64 = _fill("tk_fill_exponential_f64", 8)
 tk_fill_exponential_f32 = _fill("tk_fill_exponential_f32", 4)
 tk_philox_fill_u32 = _fill("tk_philox_fill_u32", 4)
 tk_philox_fill_u64 = _fill("tk_philox_fill_u64", 8)
 tk_philox_fill_f32 = _fill("tk_philox_fill_f32", 4)
 tk_philox_fill_f64 = _fill("tk_philox_fill_f64", 8)
+tk_philox_fill_normal_f32 = _fill("tk_philox_fill_normal_f32", 4)
+tk_philox_fill_normal_f64 = _fill("tk_philox_fill_normal_f64", 8)
+
+
+def tk_philox_fill_u32_below(key, start_draw, n, bound, out, stream=None):
+    _check(lib.tk_philox_fill_u32_below(key, start_draw, n, bound, _buf(out, 4, n, "tk_philox_fill_u32_below"),
+                                        _stream(stream, out)), "tk_philox_fill_u32_below")
+
+
+def tk_philox_fill_u64_below(key, start_draw, n, bound, out, stream=None):
+    _check(lib.tk_philox_fill_u64_below(key, start_draw, n, bound, _buf(out, 8, n, "tk_philox_fill_u64_below"),
+                                        _stream(stream, out)), "tk_philox_fill_u64_below")
 
 
 def tk_fill_u32_below(key, start_draw, n, bound, out, stream=None):
@@ -236,6 +257,11 @@ def tk_alias_build_host(weights):
 def tk_fill_choice_u32(key, start_draw, n, table, out, stream=None):
     _check(lib.tk_fill_choice_u32(key, start_draw, n, table.handle, _buf(out, 4, n, "tk_fill_choice_u32"),
                                   _stream(stream, out)), "tk_fill_choice_u32")
+
+
+def tk_philox_fill_choice_u32(key, start_draw, n, table, out, stream=None):
+    _check(lib.tk_philox_fill_choice_u32(key, start_draw, n, table.handle, _buf(out, 4, n, "tk_philox_fill_choice_u32"),
+                                         _stream(stream, out)), "tk_philox_fill_choice_u32")
 
 
 def tk_ziggurat_table():

@@ -73,7 +73,8 @@ struct ChoiceArgs {
   uint32_t *out;
   uint64_t start, head, nvec;
   uint32_t tail;
-  uint32_t hk;
+  uint32_t hk;      // lowbias32 source: hash of the key
+  uint32_t k0, k1;  // Philox source: the key
   uint32_t n;
   const uint2 *table;
 };
@@ -85,79 +86,142 @@ __device__ __forceinline__ uint32_t choose(const ChoiceArgs &a, const uint2 *tab
   return lo < e.x ? col : e.y;
 }
 
-template <bool kLds>
+template <bool kLds, bool kPhilox>
 __device__ __forceinline__ uint32_t choice_elem(const ChoiceArgs &a, const uint2 *tab, uint64_t k) {
+  if (kPhilox) {
+    const uint64_t w = 2 * (a.start + k);
+    return choose<kLds>(a, tab, philox_word(w, a.k0, a.k1), philox_word(w + 1, a.k0, a.k1));
+  }
   const uint32_t c = 2u * (uint32_t)(a.start + k);
   return choose<kLds>(a, tab, word(a.hk, c), word(a.hk, c + 1));
 }
 
+// The eight Philox words w0 .. w0+7 of a lane whose neighbour starts at w0 + 8 (word
+// offset w0 & 3 is 0 or 2, the same for every lane).  At offset 2 the last two words are
+// the first two of the next lane's block, handed over by ds_bpermute; lane 63 computes
+// them.  Every lane of the wave must call this.
+__device__ __forceinline__ void philox_words8(uint64_t w0, uint32_t k0, uint32_t k1, uint32_t w[8]) {
+  const uint64_t b = w0 >> 2;
+  const U32x4 B0 = philox4x32_10(b, k0, k1), B1 = philox4x32_10(b + 1, k0, k1);
+  if ((w0 & 3u) == 0) {
+    w[0] = B0.a; w[1] = B0.b; w[2] = B0.c; w[3] = B0.d;
+    w[4] = B1.a; w[5] = B1.b; w[6] = B1.c; w[7] = B1.d;
+    return;
+  }
+  uint32_t n0 = from_next_lane(B0.a), n1 = from_next_lane(B0.b);
+  if (lane_id() == 63) {
+    const U32x4 B2 = philox4x32_10(b + 2, k0, k1);
+    n0 = B2.a; n1 = B2.b;
+  }
+  w[0] = B0.c; w[1] = B0.d; w[2] = B1.a; w[3] = B1.b;
+  w[4] = B1.c; w[5] = B1.d; w[6] = n0; w[7] = n1;
+}
+
 // Vector v: four indices from the eight words c0 .. c0+7, c0 = 2 (start + head + 4v).  When
 // start + head is a multiple of 4, c0 is a multiple of 8 and (c0 + j) ^ hk = c0 ^ (hk ^ j).
-template <bool kLds, bool kAligned8, bool kCheck, bool kNT>
+// Philox: the same four draws from Philox words 2 (start + head + 4v) ...; the whole wave
+// computes its words before the range check, since the hand-over needs every lane.
+template <bool kLds, bool kAligned8, bool kCheck, bool kNT, bool kPhilox>
 __device__ __forceinline__ void choice_vec(const ChoiceArgs &a, const uint2 *tab, uint64_t v) {
-  if (kCheck && v >= a.nvec) return;
-  const uint32_t c0 = 2u * (uint32_t)(a.start + a.head + 4 * v);
   uint32_t r[4];
+  if (kPhilox) {
+    uint32_t w[8];
+    philox_words8(2 * (a.start + a.head + 4 * v), a.k0, a.k1, w);
+    if (kCheck && v >= a.nvec) return;
 #pragma unroll
-  for (uint32_t j = 0; j < 4; ++j) {
-    const uint32_t lo = kAligned8 ? lowbias32(c0 ^ (a.hk ^ (2 * j))) : word(a.hk, c0 + 2 * j);
-    const uint32_t hi = kAligned8 ? lowbias32(c0 ^ (a.hk ^ (2 * j + 1))) : word(a.hk, c0 + 2 * j + 1);
-    r[j] = choose<kLds>(a, tab, lo, hi);
+    for (uint32_t j = 0; j < 4; ++j) r[j] = choose<kLds>(a, tab, w[2 * j], w[2 * j + 1]);
+  } else {
+    if (kCheck && v >= a.nvec) return;
+    const uint32_t c0 = 2u * (uint32_t)(a.start + a.head + 4 * v);
+#pragma unroll
+    for (uint32_t j = 0; j < 4; ++j) {
+      const uint32_t lo = kAligned8 ? lowbias32(c0 ^ (a.hk ^ (2 * j))) : word(a.hk, c0 + 2 * j);
+      const uint32_t hi = kAligned8 ? lowbias32(c0 ^ (a.hk ^ (2 * j + 1))) : word(a.hk, c0 + 2 * j + 1);
+      r[j] = choose<kLds>(a, tab, lo, hi);
+    }
   }
   store16<kNT>(a.out + a.head + 4 * v, make_uint4(r[0], r[1], r[2], r[3]));
 }
 
-template <int T, bool kLds, bool kAligned8, bool kNT>
+template <int T, bool kLds, bool kAligned8, bool kNT, bool kPhilox>
 __device__ __forceinline__ void choice_tiles(const ChoiceArgs &a, const uint2 *tab) {
   const uint64_t v0 = (uint64_t)blockIdx.x * T * kBlock + threadIdx.x;
   if ((uint64_t)(blockIdx.x + 1) * T * kBlock <= a.nvec) {
-    for (int t = 0; t < T; ++t) choice_vec<kLds, kAligned8, false, kNT>(a, tab, v0 + (uint64_t)t * kBlock);
+    for (int t = 0; t < T; ++t) choice_vec<kLds, kAligned8, false, kNT, kPhilox>(a, tab, v0 + (uint64_t)t * kBlock);
   } else {
-    for (int t = 0; t < T; ++t) choice_vec<kLds, kAligned8, true, kNT>(a, tab, v0 + (uint64_t)t * kBlock);
+    for (int t = 0; t < T; ++t) choice_vec<kLds, kAligned8, true, kNT, kPhilox>(a, tab, v0 + (uint64_t)t * kBlock);
   }
 }
 
 // T consecutive 4 KiB tiles per work-group over a one-shot grid; with kLds the table is
 // copied to LDS once per group.
-template <int T, bool kLds, bool kNT>
+template <int T, bool kLds, bool kNT, bool kPhilox>
 __global__ __launch_bounds__(kBlock) void k_choice(ChoiceArgs a) {
   extern __shared__ uint2 tab[];
   if (kLds) {
     for (uint32_t i = threadIdx.x; i < a.n; i += kBlock) tab[i] = a.table[i];
     __syncthreads();
   }
-  if (((a.start + a.head) & 3u) == 0) choice_tiles<T, kLds, true, kNT>(a, tab);
-  else choice_tiles<T, kLds, false, kNT>(a, tab);
+  if (((a.start + a.head) & 3u) == 0) choice_tiles<T, kLds, true, kNT, kPhilox>(a, tab);
+  else choice_tiles<T, kLds, false, kNT, kPhilox>(a, tab);
   if (blockIdx.x == 0) {
     const uint32_t t = threadIdx.x;
-    if (t < a.head) a.out[t] = choice_elem<kLds>(a, tab, t);
+    if (t < a.head) a.out[t] = choice_elem<kLds, kPhilox>(a, tab, t);
     if (t >= 128 && t - 128 < a.tail) {
       const uint64_t k = a.head + 4 * a.nvec + (t - 128);
-      a.out[k] = choice_elem<kLds>(a, tab, k);
+      a.out[k] = choice_elem<kLds, kPhilox>(a, tab, k);
     }
   }
 }
 
-template <int T, bool kLds>
+template <int T, bool kLds, bool kPhilox>
 static void launch_choice_t(const ChoiceArgs &a, uint32_t grid, hipStream_t stream) {
   const size_t lds = kLds ? (size_t)a.n * sizeof(uint2) : 0;
   if (config().nt_stores)
-    hipLaunchKernelGGL((k_choice<T, kLds, true>), dim3(grid), dim3(kBlock), lds, stream, a);
+    hipLaunchKernelGGL((k_choice<T, kLds, true, kPhilox>), dim3(grid), dim3(kBlock), lds, stream, a);
   else
-    hipLaunchKernelGGL((k_choice<T, kLds, false>), dim3(grid), dim3(kBlock), lds, stream, a);
+    hipLaunchKernelGGL((k_choice<T, kLds, false, kPhilox>), dim3(grid), dim3(kBlock), lds, stream, a);
 }
 
-template <bool kLds>
+template <bool kLds, bool kPhilox>
 static void launch_choice(const ChoiceArgs &a, int tiles, hipStream_t stream) {
   const uint64_t per_group = (uint64_t)kBlock * tiles;
   uint64_t groups = (a.nvec + per_group - 1) / per_group;
   if (groups == 0) groups = 1;
   switch (tiles) {
-    case 1: launch_choice_t<1, kLds>(a, (uint32_t)groups, stream); break;
-    case 2: launch_choice_t<2, kLds>(a, (uint32_t)groups, stream); break;
-    case 8: launch_choice_t<8, kLds>(a, (uint32_t)groups, stream); break;
-    default: launch_choice_t<4, kLds>(a, (uint32_t)groups, stream); break;
+    case 1: launch_choice_t<1, kLds, kPhilox>(a, (uint32_t)groups, stream); break;
+    case 2: launch_choice_t<2, kLds, kPhilox>(a, (uint32_t)groups, stream); break;
+    case 8: launch_choice_t<8, kLds, kPhilox>(a, (uint32_t)groups, stream); break;
+    default: launch_choice_t<4, kLds, kPhilox>(a, (uint32_t)groups, stream); break;
   }
+}
+
+// Validates and launches a choice fill; the caller has set the source fields of `a`.
+template <bool kPhilox>
+static tk_status choice_fill(ChoiceArgs a, uint64_t start_draw, uint64_t n, uint64_t max_draw, const tk_alias *table,
+                             uint32_t *out, hipStream_t stream) {
+  if (!table) return TK_EINVAL;
+  if (n == 0) return TK_OK;
+  if (!out || ((uintptr_t)out & 3u)) return TK_EINVAL;
+  if (start_draw > max_draw || n - 1 > max_draw - start_draw) return TK_ERANGE;
+  tk_status st;
+  const int dev = current_device(&st);
+  if (dev < 0) return st;
+  if (dev != table->device) return TK_EINVAL;
+  a.out = out;
+  a.start = start_draw;
+  const uint64_t mis = (uintptr_t)out & 15u;
+  a.head = mis ? (16 - mis) / 4 : 0;
+  if (a.head > n) a.head = n;
+  a.nvec = (n - a.head) / 4;
+  a.tail = (uint32_t)(n - a.head - 4 * a.nvec);
+  a.n = table->n;
+  a.table = table->table;
+  const int zt = config().choice_tiles;
+  const int tiles = zt >= 8 ? 8 : zt >= 4 ? 4 : zt >= 2 ? 2 : 1;
+  if (a.n <= kChoiceLdsMax) launch_choice<true, kPhilox>(a, tiles, stream);
+  else launch_choice<false, kPhilox>(a, tiles, stream);
+  return launch_status();
 }
 
 }  // namespace tk
@@ -230,32 +294,17 @@ tk_status tk_alias_export(const tk_alias *t, uint32_t *q, uint32_t *alias) {
 
 tk_status tk_fill_choice_u32(uint32_t key, uint64_t start_draw, uint64_t n, const tk_alias *table, uint32_t *out,
                              hipStream_t stream) {
-  if (!table) return TK_EINVAL;
-  if (n == 0) return TK_OK;
-  if (!out || ((uintptr_t)out & 3u)) return TK_EINVAL;
-  if (start_draw > 0x7FFFFFFFull || n - 1 > 0x7FFFFFFFull - start_draw) return TK_ERANGE;
-  tk_status st;
-  const int dev = current_device(&st);
-  if (dev < 0) return st;
-  if (dev != table->device) return TK_EINVAL;
-
   ChoiceArgs a{};
-  a.out = out;
-  a.start = start_draw;
-  const uint64_t mis = (uintptr_t)out & 15u;
-  a.head = mis ? (16 - mis) / 4 : 0;
-  if (a.head > n) a.head = n;
-  a.nvec = (n - a.head) / 4;
-  a.tail = (uint32_t)(n - a.head - 4 * a.nvec);
   a.hk = host_lowbias32(key);
-  a.n = table->n;
-  a.table = table->table;
+  return choice_fill<false>(a, start_draw, n, 0x7FFFFFFFull, table, out, stream);
+}
 
-  const int zt = config().choice_tiles;
-  const int tiles = zt >= 8 ? 8 : zt >= 4 ? 4 : zt >= 2 ? 2 : 1;
-  if (a.n <= kChoiceLdsMax) launch_choice<true>(a, tiles, stream);
-  else launch_choice<false>(a, tiles, stream);
-  return launch_status();
+tk_status tk_philox_fill_choice_u32(uint64_t key, uint64_t start_draw, uint64_t n, const tk_alias *table,
+                                    uint32_t *out, hipStream_t stream) {
+  ChoiceArgs a{};
+  a.k0 = (uint32_t)key;
+  a.k1 = (uint32_t)(key >> 32);
+  return choice_fill<true>(a, start_draw, n, 0x7FFFFFFFFFFFFFFFull, table, out, stream);
 }
 
 }  // extern "C"

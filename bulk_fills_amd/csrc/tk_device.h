@@ -136,8 +136,9 @@ struct U32x4 {
   uint32_t a, b, c, d;
 };
 
-__device__ __forceinline__ U32x4 philox4x32_10(uint64_t block, uint32_t k0, uint32_t k1) {
-  uint32_t c0 = (uint32_t)block, c1 = (uint32_t)(block >> 32), c2 = 0, c3 = 0;
+// The block with counter (c0, c1, c2, c3) under key (k0, k1).
+__device__ __forceinline__ U32x4 philox4x32_10_ctr(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t k0,
+                                                   uint32_t k1) {
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
     uint64_t p0 = (uint64_t)0xD2511F53u * c0;
@@ -153,6 +154,85 @@ __device__ __forceinline__ U32x4 philox4x32_10(uint64_t block, uint32_t k0, uint
     k1 += 0xBB67AE85u;
   }
   return {c0, c1, c2, c3};
+}
+
+// Primary block b: counter (lo32 b, hi32 b, 0, 0).
+__device__ __forceinline__ U32x4 philox4x32_10(uint64_t block, uint32_t k0, uint32_t k1) {
+  return philox4x32_10_ctr((uint32_t)block, (uint32_t)(block >> 32), 0u, 0u, k0, k1);
+}
+
+__device__ __forceinline__ uint32_t lane_of(const U32x4 &b, uint32_t j) {
+  return j == 0 ? b.a : j == 1 ? b.b : j == 2 ? b.c : b.d;
+}
+
+// The Philox substream of draw i for purpose P: word j is lane j & 3 of the block with
+// counter (lo32 i, hi32 i, P, j >> 2), disjoint from the primary blocks (counter words 2
+// and 3 zero).  Nothing is computed until the first word is asked for, so a rejection
+// loop that never runs costs nothing.
+struct PhiloxSub {
+  uint32_t k0, k1, c0, c1, purpose, pos;
+  U32x4 blk;
+  __device__ __forceinline__ PhiloxSub(uint32_t key0, uint32_t key1, uint64_t i, uint32_t p)
+      : k0(key0), k1(key1), c0((uint32_t)i), c1((uint32_t)(i >> 32)), purpose(p), pos(0), blk{0, 0, 0, 0} {}
+  __device__ __forceinline__ uint32_t next32() {
+    if ((pos & 3u) == 0) blk = philox4x32_10_ctr(c0, c1, purpose, pos >> 2, k0, k1);
+    return lane_of(blk, pos++ & 3u);
+  }
+  __device__ __forceinline__ uint64_t next64() {
+    const uint32_t lo = next32(), hi = next32();
+    return (uint64_t)lo | ((uint64_t)hi << 32);
+  }
+};
+
+// Lemire's step with retries from a substream object (next32 / next64), for sources whose
+// substream needs no set-up (Philox).
+template <class Sub>
+__device__ __forceinline__ uint32_t lemire32_sub(uint32_t x, uint32_t s, uint32_t t, Sub sub) {
+  uint64_t m = (uint64_t)x * s;
+  if (__builtin_expect((uint32_t)m < t, 0)) {
+    for (uint32_t j = 0; j < kSubstreamCap; ++j) {
+      m = (uint64_t)sub.next32() * s;
+      if ((uint32_t)m >= t) break;
+    }
+  }
+  return (uint32_t)(m >> 32);
+}
+
+template <bool kSmall, class Sub>
+__device__ __forceinline__ uint64_t lemire64_sub(uint64_t x, uint64_t s, uint64_t t, Sub sub) {
+  uint64_t lo;
+  uint64_t hi = mul_hi_lo<kSmall>(x, s, &lo);
+  if (__builtin_expect(lo < t, 0)) {
+    for (uint32_t j = 0; j < kSubstreamCap; ++j) {
+      hi = mul_hi_lo<kSmall>(sub.next64(), s, &lo);
+      if (lo >= t) break;
+    }
+  }
+  return hi;
+}
+
+// Four consecutive Philox words starting at word w0 (word offset w0 & 3 uniform across the
+// launch, and the next lane's w0 four words on): the lane's own block plus, at unaligned
+// offsets, the head of the next lane's.  Every lane of the wave must call this.
+__device__ __forceinline__ uint4 philox_words(uint64_t w0, uint32_t k0, uint32_t k1) {
+  const uint64_t b = w0 >> 2;
+  const uint32_t o = (uint32_t)(w0 & 3u);
+  U32x4 B = philox4x32_10(b, k0, k1);
+  if (o == 0) return make_uint4(B.a, B.b, B.c, B.d);
+  uint32_t n0 = from_next_lane(B.a), n1 = from_next_lane(B.b), n2 = from_next_lane(B.c);
+  if (lane_id() == 63) {
+    U32x4 N = philox4x32_10(b + 1, k0, k1);
+    n0 = N.a; n1 = N.b; n2 = N.c;
+  }
+  if (o == 1) return make_uint4(B.b, B.c, B.d, n0);
+  if (o == 2) return make_uint4(B.c, B.d, n0, n1);
+  return make_uint4(B.d, n0, n1, n2);
+}
+
+__device__ __forceinline__ uint32_t philox_word(uint64_t w, uint32_t k0, uint32_t k1) {
+  U32x4 B = philox4x32_10(w >> 2, k0, k1);
+  const uint32_t o = (uint32_t)(w & 3u);
+  return o == 0 ? B.a : o == 1 ? B.b : o == 2 ? B.c : B.d;
 }
 
 // ---- stores ----------------------------------------------------------------------------

@@ -258,14 +258,19 @@ struct OpBelow64 : FillBase<T> {
 // ---------------------------------------------------------------------------------------
 // f32 normal: Box-Muller pairs (draw i belongs to pair i >> 1; even i cos, odd i sin)
 // ---------------------------------------------------------------------------------------
+template <bool kHalfTurn>
 struct OpNormalF32 : FillBase<float> {
   uint32_t hk;
-  // Pair c is the public API's tk_randn2_f32: r = sqrt(-2 ln(1 - u1)) with the hardware
-  // base-2 logarithm (ln x = ln 2 * log2 x) and square root; cos and sin of 2 pi t with the
-  // hardware sine and cosine, which take their argument in turns, so the wrapped t in
-  // [-1/2, 1/2) goes in unscaled.  Measured on MI355X over every 2^-23 grid value: radius
-  // error <= 4.7e-7, sine and cosine error <= 1.3e-7, so |error| <= 1.2e-6 for |x| < 5.65.
-  __device__ __forceinline__ void pair(uint32_t c, float *cs, float *sn) const { tk_randn2_f32(hk, c, cs, sn); }
+  // Pair c is the public API's tk_randn2_f32 (or its half-turn form): r = sqrt(-2 ln(1 - u1))
+  // with the hardware base-2 logarithm (ln x = ln 2 * log2 x) and square root; cos and sin
+  // of 2 pi t with the hardware sine and cosine, which take their argument in turns, so t
+  // in [-1/2, 1/2) goes in unscaled.  Measured on MI355X over every 2^-23 grid value:
+  // radius error <= 4.7e-7, sine and cosine error <= 1.3e-7, so |error| <= 1.2e-6 for
+  // |x| < 5.65.
+  __device__ __forceinline__ void pair(uint32_t c, float *cs, float *sn) const {
+    if (kHalfTurn) tk_box_muller_half_turn_f32(word(hk, 2u * c), word(hk, 2u * c + 1u), cs, sn);
+    else tk_randn2_f32(hk, c, cs, sn);
+  }
   __device__ __forceinline__ float elem(uint64_t k) const {
     const uint64_t i = start + k;
     float c, s;
@@ -287,6 +292,17 @@ struct OpNormalF32 : FillBase<float> {
       pair(c0 + 2, &e, &s_unused);
     }
     return u4(__float_as_uint(b), __float_as_uint(c), __float_as_uint(d), __float_as_uint(e));
+  }
+};
+
+// One normal per counter (Phobos, §randn): element i is the cosine of pair i.
+struct OpRandnF32 : FillBase<float> {
+  uint32_t hk;
+  __device__ __forceinline__ float elem(uint64_t k) const { return tk_randn_f32(hk, (uint32_t)(start + k)); }
+  __device__ __forceinline__ uint4 vec(uint64_t v) const {
+    const uint32_t c = (uint32_t)vec_draw(v);
+    return u4(__float_as_uint(tk_randn_f32(hk, c)), __float_as_uint(tk_randn_f32(hk, c + 1)),
+              __float_as_uint(tk_randn_f32(hk, c + 2)), __float_as_uint(tk_randn_f32(hk, c + 3)));
   }
 };
 
@@ -373,29 +389,6 @@ struct OpDropout : FillBase<float> {
 // ---------------------------------------------------------------------------------------
 // Philox4x32-10 word source
 // ---------------------------------------------------------------------------------------
-// Four consecutive Philox words starting at word w0 (word offset w0 & 3 uniform across the
-// launch): the lane's own block plus, at unaligned offsets, the head of the next lane's.
-__device__ __forceinline__ uint4 philox_words(uint64_t w0, uint32_t k0, uint32_t k1) {
-  const uint64_t b = w0 >> 2;
-  const uint32_t o = (uint32_t)(w0 & 3u);
-  U32x4 B = philox4x32_10(b, k0, k1);
-  if (o == 0) return u4(B.a, B.b, B.c, B.d);
-  uint32_t n0 = from_next_lane(B.a), n1 = from_next_lane(B.b), n2 = from_next_lane(B.c);
-  if (lane_id() == 63) {
-    U32x4 N = philox4x32_10(b + 1, k0, k1);
-    n0 = N.a; n1 = N.b; n2 = N.c;
-  }
-  if (o == 1) return u4(B.b, B.c, B.d, n0);
-  if (o == 2) return u4(B.c, B.d, n0, n1);
-  return u4(B.d, n0, n1, n2);
-}
-
-__device__ __forceinline__ uint32_t philox_word(uint64_t w, uint32_t k0, uint32_t k1) {
-  U32x4 B = philox4x32_10(w >> 2, k0, k1);
-  const uint32_t o = (uint32_t)(w & 3u);
-  return o == 0 ? B.a : o == 1 ? B.b : o == 2 ? B.c : B.d;
-}
-
 template <bool kFloat>
 struct OpPhilox32 : FillBase<uint32_t> {
   uint32_t k0, k1;
@@ -422,6 +415,71 @@ struct OpPhilox64 : FillBase<uint64_t> {
     uint4 w = philox_words(2 * vec_draw(v), k0, k1);
     uint64_t a = xf(w.x, w.y), b = xf(w.z, w.w);
     return u4(lo32(a), hi32(a), lo32(b), hi32(b));
+  }
+};
+
+// ---------------------------------------------------------------------------------------
+// Philox variants of the bounded and normal fills: the definitions above over Philox
+// words; a rejected draw i continues on PhiloxSub(i, purpose)
+// ---------------------------------------------------------------------------------------
+struct OpPhiloxBelow32 : FillBase<uint32_t> {
+  uint32_t k0, k1, s, t;
+  __device__ __forceinline__ uint32_t one(uint32_t w, uint64_t i) const {
+    return lemire32_sub(w, s, t, PhiloxSub(k0, k1, i, kPurposeBelow32));
+  }
+  __device__ __forceinline__ uint32_t elem(uint64_t k) const { return one(philox_word(start + k, k0, k1), start + k); }
+  __device__ __forceinline__ uint4 vec(uint64_t v) const {
+    const uint64_t i = vec_draw(v);
+    const uint4 w = philox_words(i, k0, k1);
+    return u4(one(w.x, i), one(w.y, i + 1), one(w.z, i + 2), one(w.w, i + 3));
+  }
+};
+
+template <bool kSmall>
+struct OpPhiloxBelow64 : FillBase<uint64_t> {
+  uint32_t k0, k1;
+  uint64_t s, t;
+  __device__ __forceinline__ uint64_t one(uint32_t lo, uint32_t hi, uint64_t i) const {
+    return lemire64_sub<kSmall>((uint64_t)lo | ((uint64_t)hi << 32), s, t, PhiloxSub(k0, k1, i, kPurposeBelow64));
+  }
+  __device__ __forceinline__ uint64_t elem(uint64_t k) const {
+    const uint64_t i = start + k;
+    return one(philox_word(2 * i, k0, k1), philox_word(2 * i + 1, k0, k1), i);
+  }
+  __device__ __forceinline__ uint4 vec(uint64_t v) const {
+    const uint64_t i = vec_draw(v);
+    const uint4 w = philox_words(2 * i, k0, k1);
+    const uint64_t a = one(w.x, w.y, i), b = one(w.z, w.w, i + 1);
+    return u4(lo32(a), hi32(a), lo32(b), hi32(b));
+  }
+};
+
+// Box-Muller pairs over Philox words (pair c: words 2c and 2c+1), laid out as OpNormalF32.
+struct OpPhiloxNormalF32 : FillBase<float> {
+  uint32_t k0, k1;
+  __device__ __forceinline__ void pair(uint64_t c, float *cs, float *sn) const {
+    tk_box_muller_f32(philox_word(2 * c, k0, k1), philox_word(2 * c + 1, k0, k1), cs, sn);
+  }
+  __device__ __forceinline__ float elem(uint64_t k) const {
+    const uint64_t i = start + k;
+    float c, s;
+    pair(i >> 1, &c, &s);
+    return (i & 1u) ? s : c;
+  }
+  __device__ __forceinline__ uint4 vec(uint64_t v) const {
+    const uint64_t i0 = vec_draw(v);
+    const uint64_t c0 = i0 >> 1;
+    const uint4 w = philox_words(2 * c0, k0, k1);  // pairs c0 and c0 + 1 (word offset 0 or 2, uniform)
+    float a, b, c, d;
+    tk_box_muller_f32(w.x, w.y, &a, &b);
+    tk_box_muller_f32(w.z, w.w, &c, &d);
+    if ((i0 & 1u) == 0) return u4(__float_as_uint(a), __float_as_uint(b), __float_as_uint(c), __float_as_uint(d));
+    float e = from_next_lane(a);  // the next lane's first pair is c0 + 2
+    if (lane_id() == 63) {
+      float s_unused;
+      pair(c0 + 2, &e, &s_unused);
+    }
+    return u4(__float_as_uint(b), __float_as_uint(c), __float_as_uint(d), __float_as_uint(e));
   }
 };
 
@@ -595,7 +653,22 @@ tk_status tk_fill_i64_below(uint32_t key, uint64_t start_draw, uint64_t n, int64
 
 tk_status tk_fill_normal_f32(uint32_t key, uint64_t start_draw, uint64_t n, float *out, hipStream_t stream) {
   TK_PRECHECK(out, kMaxW32);
-  OpNormalF32 op{};
+  OpNormalF32<false> op{};
+  op.hk = host_lowbias32(key);
+  return run_simple(op, out, start_draw, n, stream);
+}
+
+tk_status tk_fill_normal_f32_half_turn(uint32_t key, uint64_t start_draw, uint64_t n, float *out,
+                                       hipStream_t stream) {
+  TK_PRECHECK(out, kMaxW32);
+  OpNormalF32<true> op{};
+  op.hk = host_lowbias32(key);
+  return run_simple(op, out, start_draw, n, stream);
+}
+
+tk_status tk_fill_randn_f32(uint32_t key, uint64_t start_draw, uint64_t n, float *out, hipStream_t stream) {
+  TK_PRECHECK(out, kMaxW64);  // counter c reads words 2c and 2c + 1
+  OpRandnF32 op{};
   op.hk = host_lowbias32(key);
   return run_simple(op, out, start_draw, n, stream);
 }
@@ -659,6 +732,39 @@ tk_status tk_philox_fill_f32(uint64_t key, uint64_t start_draw, uint64_t n, floa
 tk_status tk_philox_fill_u64(uint64_t key, uint64_t start_draw, uint64_t n, uint64_t *out, hipStream_t stream) {
   TK_PRECHECK(out, kMaxPhilox64);
   OpPhilox64<false> op{};
+  op.k0 = (uint32_t)key; op.k1 = (uint32_t)(key >> 32);
+  return run_simple(op, out, start_draw, n, stream);
+}
+
+tk_status tk_philox_fill_u32_below(uint64_t key, uint64_t start_draw, uint64_t n, uint32_t bound, uint32_t *out,
+                                   hipStream_t stream) {
+  if (bound == 0) return TK_EINVAL;
+  TK_PRECHECK(out, ~0ull);
+  OpPhiloxBelow32 op{};
+  op.k0 = (uint32_t)key; op.k1 = (uint32_t)(key >> 32);
+  op.s = bound;
+  op.t = (uint32_t)(0u - bound) % bound;
+  return run_simple(op, out, start_draw, n, stream);
+}
+
+tk_status tk_philox_fill_u64_below(uint64_t key, uint64_t start_draw, uint64_t n, uint64_t bound, uint64_t *out,
+                                   hipStream_t stream) {
+  if (bound == 0) return TK_EINVAL;
+  TK_PRECHECK(out, kMaxPhilox64);
+  const uint64_t t = (0ull - bound) % bound;
+  if (bound <= 0xFFFFFFFFull) {
+    OpPhiloxBelow64<true> op{};
+    op.k0 = (uint32_t)key; op.k1 = (uint32_t)(key >> 32); op.s = bound; op.t = t;
+    return run_simple(op, out, start_draw, n, stream);
+  }
+  OpPhiloxBelow64<false> op{};
+  op.k0 = (uint32_t)key; op.k1 = (uint32_t)(key >> 32); op.s = bound; op.t = t;
+  return run_simple(op, out, start_draw, n, stream);
+}
+
+tk_status tk_philox_fill_normal_f32(uint64_t key, uint64_t start_draw, uint64_t n, float *out, hipStream_t stream) {
+  TK_PRECHECK(out, ~0ull);
+  OpPhiloxNormalF32 op{};
   op.k0 = (uint32_t)key; op.k1 = (uint32_t)(key >> 32);
   return run_simple(op, out, start_draw, n, stream);
 }

@@ -44,8 +44,9 @@ struct ZigArgs {
   uint64_t head;   // 0 or 1 element before the first 16-byte boundary
   uint64_t nvec;   // whole 16-byte vectors (two elements each)
   uint32_t tail;   // 0 or 1 element after them
-  uint32_t hk;     // lowbias32(key)
-  uint32_t hkp;    // lowbias32(sub(key, NORM))
+  uint32_t hk;     // lowbias32 source: lowbias32(key)
+  uint32_t hkp;    //   and lowbias32(sub(key, NORM))
+  uint32_t k0, k1; // Philox source: the key
   const double2 *xx;  // {X[L] * 2^-53, X[L+1]}, L < 1024
   const double *f;    // F[0 .. 1024]
   double r;
@@ -81,15 +82,36 @@ __device__ __forceinline__ bool zig_fast(const double2 *tab, uint32_t lo, uint32
 
 // The four words of vector v: counters c0 .. c0+3 with c0 = 2 (start + head + 2v).  When
 // start + head is even, c0 is a multiple of 4 and (c0 + j) ^ hk = c0 ^ (hk ^ j), one xor
-// with a uniform value per word.
-template <bool kAligned4>
-__device__ __forceinline__ void zig_words(uint32_t hk, uint32_t c0, uint32_t w[4]) {
+// with a uniform value per word.  Philox: the lane's block, or at odd start + head its
+// second half and the next lane's first (every lane of the wave must call this).
+template <bool kAligned4, bool kPhilox>
+__device__ __forceinline__ void zig_words(const ZigArgs &a, uint64_t v, uint32_t w[4]) {
+  if (kPhilox) {
+    const uint4 b = philox_words(2 * (a.start + a.head + 2 * v), a.k0, a.k1);
+    w[0] = b.x; w[1] = b.y; w[2] = b.z; w[3] = b.w;
+    return;
+  }
+  const uint32_t c0 = 2u * (uint32_t)(a.start + a.head + 2 * v);
   if (kAligned4) {
 #pragma unroll
-    for (uint32_t j = 0; j < 4; ++j) w[j] = lowbias32(c0 ^ (hk ^ j));
+    for (uint32_t j = 0; j < 4; ++j) w[j] = lowbias32(c0 ^ (a.hk ^ j));
   } else {
 #pragma unroll
-    for (uint32_t j = 0; j < 4; ++j) w[j] = word(hk, c0 + j);
+    for (uint32_t j = 0; j < 4; ++j) w[j] = word(a.hk, c0 + j);
+  }
+}
+
+// The primary 64-bit draw of element k: words 2i (lo) and 2i+1 (hi), i = start + k.
+template <bool kPhilox>
+__device__ __forceinline__ void zig_primary(const ZigArgs &a, uint64_t k, uint32_t *lo, uint32_t *hi) {
+  if (kPhilox) {
+    const uint64_t w = 2 * (a.start + k);
+    *lo = philox_word(w, a.k0, a.k1);
+    *hi = philox_word(w + 1, a.k0, a.k1);
+  } else {
+    const uint32_t c = 2u * (uint32_t)(a.start + k);
+    *lo = word(a.hk, c);
+    *hi = word(a.hk, c + 1);
   }
 }
 
@@ -126,6 +148,7 @@ __device__ __forceinline__ void enqueue2(bool p0, bool p1, uint32_t k0, uint32_t
                       k0 + 1, q, cap, a);
 }
 
+template <bool kPhilox>
 __device__ double zig_slow(const ZigArgs &a, uint64_t k);
 
 // Table pass: T consecutive 4 KiB tiles per work-group.  With kLds the 16 KiB layer table
@@ -138,12 +161,12 @@ __device__ double zig_slow(const ZigArgs &a, uint64_t k);
 // group's slot for the continuation pass.
 // One tile: 256 lanes, two elements each.  kCheck guards vectors past the end (only the
 // last group needs it).
-template <bool kAligned4, bool kCheck, bool kFused, bool kNT>
+template <bool kAligned4, bool kCheck, bool kFused, bool kNT, bool kPhilox>
 __device__ __forceinline__ void zig_tile(const ZigArgs &a, const double2 *tab, uint64_t v, uint32_t *q,
                                          uint32_t *qn, uint32_t cap) {
   const bool in = !kCheck || v < a.nvec;
   uint32_t w[4];
-  zig_words<kAligned4>(a.hk, 2u * (uint32_t)(a.start + a.head + 2 * v), w);
+  zig_words<kAligned4, kPhilox>(a, v, w);
   double y0, y1;
   const bool f0 = zig_fast(tab, w[0], w[1], &y0);
   const bool f1 = zig_fast(tab, w[2], w[3], &y1);
@@ -158,14 +181,16 @@ __device__ __forceinline__ void zig_tile(const ZigArgs &a, const double2 *tab, u
   enqueue2<kFused>(in && !f0, in && !f1, (uint32_t)(a.head + 2 * v), q, qn, cap, a);
 }
 
-template <int T, bool kAligned4, bool kFused, bool kNT>
+template <int T, bool kAligned4, bool kFused, bool kNT, bool kPhilox>
 __device__ __forceinline__ void zig_tiles(const ZigArgs &a, const double2 *tab, uint32_t *q, uint32_t *qn,
                                           uint32_t cap) {
   const uint64_t v0 = (uint64_t)blockIdx.x * T * kBlock + threadIdx.x;
   if ((uint64_t)(blockIdx.x + 1) * T * kBlock <= a.nvec) {
-    for (int t = 0; t < T; ++t) zig_tile<kAligned4, false, kFused, kNT>(a, tab, v0 + (uint64_t)t * kBlock, q, qn, cap);
+    for (int t = 0; t < T; ++t)
+      zig_tile<kAligned4, false, kFused, kNT, kPhilox>(a, tab, v0 + (uint64_t)t * kBlock, q, qn, cap);
   } else {
-    for (int t = 0; t < T; ++t) zig_tile<kAligned4, true, kFused, kNT>(a, tab, v0 + (uint64_t)t * kBlock, q, qn, cap);
+    for (int t = 0; t < T; ++t)
+      zig_tile<kAligned4, true, kFused, kNT, kPhilox>(a, tab, v0 + (uint64_t)t * kBlock, q, qn, cap);
   }
 }
 
@@ -177,7 +202,7 @@ __device__ __forceinline__ void zig_tiles(const ZigArgs &a, const double2 *tab, 
 // group that finds more (probability ~1e-10) walks its own elements again and finishes
 // every miss it meets, so nothing leaves the work-group.  Otherwise the queue goes to the
 // group's slot for the continuation pass.
-template <int T, bool kLds, bool kNT, bool kFused>
+template <int T, bool kLds, bool kNT, bool kFused, bool kPhilox>
 __global__ __launch_bounds__(kBlock) void k_zig_table_pass(ZigArgs a) {
   constexpr uint32_t kQueue = kSlotPerTile * T + (kFused ? 2u : 0u);  // fused: + block 0's edge elements
   __shared__ double2 lds_tab[kLds ? 1024 : 1];
@@ -191,8 +216,8 @@ __global__ __launch_bounds__(kBlock) void k_zig_table_pass(ZigArgs a) {
   // to the overflow list
   const uint32_t cap = kFused ? (a.slot_cap < kQueue ? a.slot_cap : kQueue) : a.slot_cap;
   const double2 *tab = kLds ? lds_tab : a.xx;
-  if (((a.start + a.head) & 1u) == 0) zig_tiles<T, true, kFused, kNT>(a, tab, q, &qn, cap);
-  else zig_tiles<T, false, kFused, kNT>(a, tab, q, &qn, cap);
+  if (((a.start + a.head) & 1u) == 0) zig_tiles<T, true, kFused, kNT, kPhilox>(a, tab, q, &qn, cap);
+  else zig_tiles<T, false, kFused, kNT, kPhilox>(a, tab, q, &qn, cap);
   if (blockIdx.x == 0) {  // the element before the first boundary and the one after the last vector
     const uint32_t t = threadIdx.x;
     bool edge = false;
@@ -201,9 +226,10 @@ __global__ __launch_bounds__(kBlock) void k_zig_table_pass(ZigArgs a) {
     if (t == 64 && a.tail) { edge = true; k = a.head + 2 * a.nvec; }
     bool fast = true;
     if (edge) {
-      const uint32_t c = 2u * (uint32_t)(a.start + k);
+      uint32_t lo, hi;
+      zig_primary<kPhilox>(a, k, &lo, &hi);
       double y;
-      fast = zig_fast(tab, word(a.hk, c), word(a.hk, c + 1), &y);
+      fast = zig_fast(tab, lo, hi, &y);
       a.out[k] = y;
     }
     enqueue2<kFused>(edge && !fast, false, (uint32_t)k, q, &qn, cap, a);
@@ -215,23 +241,27 @@ __global__ __launch_bounds__(kBlock) void k_zig_table_pass(ZigArgs a) {
     if (total <= cap) {
       for (uint32_t j = threadIdx.x; j < total; j += kBlock) {
         const uint32_t k = q[j];
-        a.out[k] = zig_slow(a, k);
+        a.out[k] = zig_slow<kPhilox>(a, k);
       }
     } else {  // more misses than the queue holds: walk the group's elements again
       const uint64_t e0 = a.head + (uint64_t)blockIdx.x * T * kBlock * 2;
       uint64_t e1 = e0 + (uint64_t)T * kBlock * 2;
       if (e1 > a.head + 2 * a.nvec) e1 = a.head + 2 * a.nvec;
       for (uint64_t k = e0 + threadIdx.x; k < e1; k += kBlock) {
-        const uint32_t c = 2u * (uint32_t)(a.start + k);
+        uint32_t lo, hi;
+        zig_primary<kPhilox>(a, k, &lo, &hi);
         double y;
-        if (!zig_fast(a.xx, word(a.hk, c), word(a.hk, c + 1), &y)) a.out[k] = zig_slow(a, k);
+        if (!zig_fast(a.xx, lo, hi, &y)) a.out[k] = zig_slow<kPhilox>(a, k);
       }
       if (blockIdx.x == 0 && threadIdx.x < 2) {  // and the edge elements
         const bool has = threadIdx.x == 0 ? a.head != 0 : a.tail != 0;
         const uint64_t k = threadIdx.x == 0 ? 0 : a.head + 2 * a.nvec;
-        const uint32_t c = 2u * (uint32_t)(a.start + k);
-        double y;
-        if (has && !zig_fast(a.xx, word(a.hk, c), word(a.hk, c + 1), &y)) a.out[k] = zig_slow(a, k);
+        if (has) {
+          uint32_t lo, hi;
+          zig_primary<kPhilox>(a, k, &lo, &hi);
+          double y;
+          if (!zig_fast(a.xx, lo, hi, &y)) a.out[k] = zig_slow<kPhilox>(a, k);
+        }
       }
     }
   } else {
@@ -241,12 +271,11 @@ __global__ __launch_bounds__(kBlock) void k_zig_table_pass(ZigArgs a) {
   }
 }
 
-// Finishes the draw of element k from its primary draw: wedge, tail and restarts all read
-// the substream split(start + k) in order.
-__device__ double zig_slow(const ZigArgs &a, uint64_t k) {
-  const uint32_t i = (uint32_t)(a.start + k);
-  uint32_t lo = word(a.hk, 2u * i), hi = word(a.hk, 2u * i + 1u);
-  Substream ss(a.hkp, i);
+// Finishes a draw (lo, hi) that left the fast path: wedge, tail and restarts read the
+// substream `ss` in order (split(i) of sub(key, NORM) for lowbias32, the NORM Philox
+// substream of draw i for Philox).
+template <class Sub>
+__device__ double zig_finish(const ZigArgs &a, uint32_t lo, uint32_t hi, Sub ss) {
   const uint32_t cap_words = 2u * kSubstreamCap;
   for (;;) {
     const uint32_t L = lo & 1023u;
@@ -279,6 +308,15 @@ __device__ double zig_slow(const ZigArgs &a, uint64_t k) {
   }
 }
 
+// Finishes element k from its primary draw.
+template <bool kPhilox>
+__device__ double zig_slow(const ZigArgs &a, uint64_t k) {
+  uint32_t lo, hi;
+  zig_primary<kPhilox>(a, k, &lo, &hi);
+  if (kPhilox) return zig_finish(a, lo, hi, PhiloxSub(a.k0, a.k1, a.start + k, kPurposeNormal64));
+  return zig_finish(a, lo, hi, Substream(a.hkp, (uint32_t)(a.start + k)));
+}
+
 // Exclusive prefix sum of v over the work-group; *total receives the sum.
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *wave_sums, uint32_t *total) {
   const int lane = lane_id(), w = (int)(threadIdx.x >> 6);
@@ -303,6 +341,7 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *w
 // Continuation pass.  Block b compacts the misses of table-pass groups
 // [b * gpb, (b + 1) * gpb) (gpb chosen so a block sees about 256 groups' worth of tiles)
 // and spreads them over its lanes, so every lane finishes about two misses.
+template <bool kPhilox>
 __global__ __launch_bounds__(kBlock) void k_zig_continue(ZigArgs a, uint32_t gpb) {
   __shared__ uint32_t s_ovf;
   __shared__ uint32_t offs[kBlock + 1];
@@ -327,19 +366,20 @@ __global__ __launch_bounds__(kBlock) void k_zig_continue(ZigArgs a, uint32_t gpb
         else hi = mid;
       }
       const uint32_t k = a.slots[(g0 + lo) * a.slot_size + (m - offs[lo])];
-      a.out[k] = zig_slow(a, k);
+      a.out[k] = zig_slow<kPhilox>(a, k);
     }
     const uint64_t gid = (uint64_t)blockIdx.x * kBlock + threadIdx.x;
     for (uint64_t j = gid; j < ovf; j += (uint64_t)gridDim.x * kBlock) {
       const uint32_t k = a.ovf[j];
-      a.out[k] = zig_slow(a, k);
+      a.out[k] = zig_slow<kPhilox>(a, k);
     }
   } else {  // the overflow list overflowed: find the misses by walking the whole fill
     const uint64_t stride = (uint64_t)gridDim.x * kBlock;
     for (uint64_t k = (uint64_t)blockIdx.x * kBlock + threadIdx.x; k < a.n; k += stride) {
-      const uint32_t c = 2u * (uint32_t)(a.start + k);
+      uint32_t lo, hi;
+      zig_primary<kPhilox>(a, k, &lo, &hi);
       double y;
-      if (!zig_fast(a.xx, word(a.hk, c), word(a.hk, c + 1), &y)) a.out[k] = zig_slow(a, k);
+      if (!zig_fast(a.xx, lo, hi, &y)) a.out[k] = zig_slow<kPhilox>(a, k);
     }
   }
 }
@@ -426,41 +466,48 @@ static tk_status zig_reserve(ZigDevice &d, uint64_t groups, uint64_t slot_words,
   return TK_OK;
 }
 
-template <int T, bool kLds, bool kFused>
+template <int T, bool kLds, bool kFused, bool kPhilox>
 static void launch_table_pass(const ZigArgs &a, hipStream_t stream) {
   if (config().nt_stores)
-    hipLaunchKernelGGL((k_zig_table_pass<T, kLds, true, kFused>), dim3(a.ngroups), dim3(kBlock), 0, stream, a);
+    hipLaunchKernelGGL((k_zig_table_pass<T, kLds, true, kFused, kPhilox>), dim3(a.ngroups), dim3(kBlock), 0, stream, a);
   else
-    hipLaunchKernelGGL((k_zig_table_pass<T, kLds, false, kFused>), dim3(a.ngroups), dim3(kBlock), 0, stream, a);
+    hipLaunchKernelGGL((k_zig_table_pass<T, kLds, false, kFused, kPhilox>), dim3(a.ngroups), dim3(kBlock), 0, stream,
+                       a);
 }
 
-template <bool kFused>
+template <bool kFused, bool kPhilox>
 static void launch_table_pass(int tiles, bool lds, const ZigArgs &a, hipStream_t stream) {
   switch (tiles) {
-    case 2: lds ? launch_table_pass<2, true, kFused>(a, stream) : launch_table_pass<2, false, kFused>(a, stream); break;
-    case 4: lds ? launch_table_pass<4, true, kFused>(a, stream) : launch_table_pass<4, false, kFused>(a, stream); break;
-    case 8: lds ? launch_table_pass<8, true, kFused>(a, stream) : launch_table_pass<8, false, kFused>(a, stream); break;
-    case 16: lds ? launch_table_pass<16, true, kFused>(a, stream) : launch_table_pass<16, false, kFused>(a, stream); break;
-    case 32: lds ? launch_table_pass<32, true, kFused>(a, stream) : launch_table_pass<32, false, kFused>(a, stream); break;
-    default: launch_table_pass<1, false, kFused>(a, stream); break;
+    case 2:
+      lds ? launch_table_pass<2, true, kFused, kPhilox>(a, stream) : launch_table_pass<2, false, kFused, kPhilox>(a, stream);
+      break;
+    case 4:
+      lds ? launch_table_pass<4, true, kFused, kPhilox>(a, stream) : launch_table_pass<4, false, kFused, kPhilox>(a, stream);
+      break;
+    case 8:
+      lds ? launch_table_pass<8, true, kFused, kPhilox>(a, stream) : launch_table_pass<8, false, kFused, kPhilox>(a, stream);
+      break;
+    case 16:
+      lds ? launch_table_pass<16, true, kFused, kPhilox>(a, stream)
+          : launch_table_pass<16, false, kFused, kPhilox>(a, stream);
+      break;
+    default: launch_table_pass<1, false, kFused, kPhilox>(a, stream); break;
   }
 }
 
-}  // namespace tk
-
-using namespace tk;
-
-extern "C" {
-
-tk_status tk_fill_normal_f64(uint32_t key, uint64_t start_draw, uint64_t n, double *out, hipStream_t stream) {
+// Validates and runs one f64 normal fill; the caller has set the source fields of `a`.
+// Element indices within one call are 32-bit (the miss queues hold them).
+template <bool kPhilox>
+static tk_status normal_f64_fill(ZigArgs a, uint64_t start_draw, uint64_t n, uint64_t max_draw, double *out,
+                                 hipStream_t stream) {
   if (n == 0) return TK_OK;
   if (!out || ((uintptr_t)out & 7u)) return TK_EINVAL;
-  if (start_draw > 0x7FFFFFFFull || n - 1 > 0x7FFFFFFFull - start_draw) return TK_ERANGE;
+  if (start_draw > max_draw || n - 1 > max_draw - start_draw) return TK_ERANGE;
+  if (n > 0xFFFFFFFFull) return TK_EINVAL;
   tk_status st;
   const int dev = current_device(&st);
   if (dev < 0) return st;
 
-  ZigArgs a{};
   a.out = out;
   a.start = start_draw;
   a.n = n;
@@ -468,8 +515,6 @@ tk_status tk_fill_normal_f64(uint32_t key, uint64_t start_draw, uint64_t n, doub
   if (a.head > n) a.head = n;
   a.nvec = (n - a.head) / 2;
   a.tail = (uint32_t)(n - a.head - 2 * a.nvec);
-  a.hk = host_lowbias32(key);
-  a.hkp = host_substream_key(key, kPurposeNormal64);
   a.r = TK_ZIG_R;
   bool fused = config().zig_fused;
   {
@@ -477,7 +522,7 @@ tk_status tk_fill_normal_f64(uint32_t key, uint64_t start_draw, uint64_t n, doub
     if (g_debug_mode) fused = g_debug_mode == 2;
   }
   const int zt = config().zig_tiles;
-  const int tiles = zt >= 32 ? 32 : zt >= 16 ? 16 : zt >= 8 ? 8 : zt >= 4 ? 4 : zt >= 2 ? 2 : 1;
+  const int tiles = zt >= 16 ? 16 : zt >= 8 ? 8 : zt >= 4 ? 4 : zt >= 2 ? 2 : 1;
   const bool lds = config().zig_lds && tiles > 1;
   const uint64_t per_group = (uint64_t)kBlock * tiles;
   uint64_t groups = (a.nvec + per_group - 1) / per_group;
@@ -505,16 +550,16 @@ tk_status tk_fill_normal_f64(uint32_t key, uint64_t start_draw, uint64_t n, doub
   a.ctr = d.ctr;
 
   if (fused) {
-    launch_table_pass<true>(tiles, lds, a, stream);
+    launch_table_pass<true, kPhilox>(tiles, lds, a, stream);
     if ((st = launch_status()) != TK_OK) return st;
   } else {
     hipLaunchKernelGGL(k_zig_reset, dim3(1), dim3(64), 0, stream, d.ctr);
     if ((st = launch_status()) != TK_OK) return st;
-    launch_table_pass<false>(tiles, lds, a, stream);
+    launch_table_pass<false, kPhilox>(tiles, lds, a, stream);
     if ((st = launch_status()) != TK_OK) return st;
     const uint32_t gpb = (uint32_t)(kBlock / tiles);  // table-pass groups per continuation block
     const uint64_t cgrid = (groups + gpb - 1) / gpb;
-    hipLaunchKernelGGL(k_zig_continue, dim3((uint32_t)cgrid), dim3(kBlock), 0, stream, a, gpb);
+    hipLaunchKernelGGL(k_zig_continue<kPhilox>, dim3((uint32_t)cgrid), dim3(kBlock), 0, stream, a, gpb);
     if ((st = launch_status()) != TK_OK) return st;
   }
   if ((st = hip_status(hipEventRecord(d.last, stream))) != TK_OK) return st;
@@ -522,6 +567,26 @@ tk_status tk_fill_normal_f64(uint32_t key, uint64_t start_draw, uint64_t n, doub
   d.last_groups = groups;
   d.last_fused = fused;
   return TK_OK;
+}
+
+}  // namespace tk
+
+using namespace tk;
+
+extern "C" {
+
+tk_status tk_fill_normal_f64(uint32_t key, uint64_t start_draw, uint64_t n, double *out, hipStream_t stream) {
+  ZigArgs a{};
+  a.hk = host_lowbias32(key);
+  a.hkp = host_substream_key(key, kPurposeNormal64);
+  return normal_f64_fill<false>(a, start_draw, n, 0x7FFFFFFFull, out, stream);
+}
+
+tk_status tk_philox_fill_normal_f64(uint64_t key, uint64_t start_draw, uint64_t n, double *out, hipStream_t stream) {
+  ZigArgs a{};
+  a.k0 = (uint32_t)key;
+  a.k1 = (uint32_t)(key >> 32);
+  return normal_f64_fill<true>(a, start_draw, n, 0x7FFFFFFFFFFFFFFFull, out, stream);
 }
 
 tk_status tk_ziggurat_table(double *x, double *f) {

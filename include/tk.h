@@ -104,6 +104,17 @@ tk_status tk_fill_i64_below(uint32_t key, uint64_t start_draw, uint64_t n, int64
 tk_status tk_fill_normal_f64(uint32_t key, uint64_t start_draw, uint64_t n, double *out, hipStream_t stream);
 tk_status tk_fill_normal_f32(uint32_t key, uint64_t start_draw, uint64_t n, float *out, hipStream_t stream);
 
+/* Normal variants (f32, i < 2^32 unless stated).
+ * half_turn: tandem-sycl, "Design", §Normals shifts the Box-Muller angle by half a turn
+ *   into [-pi, pi): the same pairs with angle 2 pi (u2 - 1/2), so both values are the
+ *   negation of tk_fill_normal_f32's.
+ * randn: Phobos, §randn, one normal per counter: element k is randn(key, start_draw + k),
+ *   the cosine of Box-Muller pair start_draw + k (words 2c and 2c+1), i.e. element
+ *   2 (start_draw + k) of tk_fill_normal_f32.  i < 2^31.                                 */
+tk_status tk_fill_normal_f32_half_turn(uint32_t key, uint64_t start_draw, uint64_t n, float *out,
+                                       hipStream_t stream);
+tk_status tk_fill_randn_f32(uint32_t key, uint64_t start_draw, uint64_t n, float *out, hipStream_t stream);
+
 /* ---- Exponentials ------------------------------------------------------------------
  * tandem-sycl, "Design", §Exponentials; tandem-cuda, "Performance", §GPU (the f32
  * exponential maps 1 - exp(-x) back to the draw's own 2^-24 grid point).  x = -ln(1 - u),
@@ -163,6 +174,24 @@ tk_status tk_philox_fill_u32(uint64_t key, uint64_t start_draw, uint64_t n, uint
 tk_status tk_philox_fill_u64(uint64_t key, uint64_t start_draw, uint64_t n, uint64_t *out, hipStream_t stream);
 tk_status tk_philox_fill_f32(uint64_t key, uint64_t start_draw, uint64_t n, float *out, hipStream_t stream);
 tk_status tk_philox_fill_f64(uint64_t key, uint64_t start_draw, uint64_t n, double *out, hipStream_t stream);
+
+/* Philox variants of the bounded, choice and normal fills: the same definitions as the
+ * lowbias32 fills above, over Philox words (u32 draw i = word i; 64-bit draw i = words 2i
+ * and 2i+1).  A draw that is rejected (Lemire) or misses the ziggurat's fast path continues
+ * on its Philox substream: word j of draw i's substream for purpose P ("BL32", "BL64",
+ * "NORM") is lane j & 3 of the block with counter (lo32 i, hi32 i, P, j >> 2), disjoint
+ * from the primary blocks.  Limits: u32_below and normal_f32 i < 2^64, u64_below, choice
+ * and normal_f64 i < 2^63; normal_f64 takes n < 2^32 per call (cut a longer fill: the
+ * pieces equal the whole).  bound == 0 is TK_EINVAL.  The choice table must be on the
+ * current device, as for tk_fill_choice_u32.                                            */
+tk_status tk_philox_fill_u32_below(uint64_t key, uint64_t start_draw, uint64_t n, uint32_t bound, uint32_t *out,
+                                   hipStream_t stream);
+tk_status tk_philox_fill_u64_below(uint64_t key, uint64_t start_draw, uint64_t n, uint64_t bound, uint64_t *out,
+                                   hipStream_t stream);
+tk_status tk_philox_fill_choice_u32(uint64_t key, uint64_t start_draw, uint64_t n, const tk_alias *table,
+                                    uint32_t *out, hipStream_t stream);
+tk_status tk_philox_fill_normal_f32(uint64_t key, uint64_t start_draw, uint64_t n, float *out, hipStream_t stream);
+tk_status tk_philox_fill_normal_f64(uint64_t key, uint64_t start_draw, uint64_t n, double *out, hipStream_t stream);
 
 /* ---- Status and introspection -------------------------------------------------------*/
 const char *tk_status_string(tk_status status);

@@ -63,18 +63,32 @@ __device__ __forceinline__ double tk_uniform_f64(uint32_t hk, uint32_t i) {
   return (double)(hi & 0x1FFFFFu) * 0x1p-21 + (double)lo * 0x1p-53;
 }
 
-/* Box-Muller pair c from the uniforms at words 2c and 2c+1 (Phobos, §randn; the pair's
- * second value is r sin): r = sqrt(-2 ln(1 - u1)) from the hardware base-2 logarithm and
- * square root, the angle 2 pi t with t = u2 wrapped into [-1/2, 1/2) through the hardware
- * sine and cosine, which take turns.  Within 1.2e-6 of the exact pair; |x| < 5.65.
- * c < 2^31. */
-__device__ __forceinline__ void tk_randn2_f32(uint32_t hk, uint32_t c, float *cos_part, float *sin_part) {
-  const float u1 = tk_uniform_f32(hk, 2u * c);
-  const float u2 = tk_uniform_f32(hk, 2u * c + 1u);
+/* Box-Muller of the f32 uniforms of words w1 and w2 (Phobos, §randn; the pair's second
+ * value is r sin): r = sqrt(-2 ln(1 - u1)) from the hardware base-2 logarithm and square
+ * root, the angle 2 pi t with t = u2 wrapped into [-1/2, 1/2) through the hardware sine
+ * and cosine, which take turns.  Within 1.2e-6 of the exact pair; |x| < 5.65. */
+__device__ __forceinline__ void tk_box_muller_f32(uint32_t w1, uint32_t w2, float *cos_part, float *sin_part) {
+  const float u1 = tk_unit23(w1), u2 = tk_unit23(w2);
   const float r = __builtin_amdgcn_sqrtf(__builtin_amdgcn_logf(1.0f - u1) * -1.38629436111989061883f);
   const float t = u2 >= 0.5f ? u2 - 1.0f : u2;
   *cos_part = r * __builtin_amdgcn_cosf(t);
   *sin_part = r * __builtin_amdgcn_sinf(t);
+}
+
+/* The same pair with the angle shifted by half a turn (tandem-sycl, "Design", §Normals):
+ * t = u2 - 1/2, so both values are the negation of tk_box_muller_f32's. */
+__device__ __forceinline__ void tk_box_muller_half_turn_f32(uint32_t w1, uint32_t w2, float *cos_part,
+                                                            float *sin_part) {
+  const float u1 = tk_unit23(w1), u2 = tk_unit23(w2);
+  const float r = __builtin_amdgcn_sqrtf(__builtin_amdgcn_logf(1.0f - u1) * -1.38629436111989061883f);
+  const float t = u2 - 0.5f;
+  *cos_part = r * __builtin_amdgcn_cosf(t);
+  *sin_part = r * __builtin_amdgcn_sinf(t);
+}
+
+/* Box-Muller pair c of key hk: the words 2c and 2c+1.  c < 2^31. */
+__device__ __forceinline__ void tk_randn2_f32(uint32_t hk, uint32_t c, float *cos_part, float *sin_part) {
+  tk_box_muller_f32(tk_word(hk, 2u * c), tk_word(hk, 2u * c + 1u), cos_part, sin_part);
 }
 
 /* One standard normal per counter (Phobos, §randn: the cosine of pair c). */

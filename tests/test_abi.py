@@ -45,7 +45,8 @@ SIMPLE = [("tk_fill_u8", 1, 1 << 34), ("tk_fill_u16", 2, 1 << 33), ("tk_fill_u32
           ("tk_fill_u64", 8, 1 << 31), ("tk_fill_f16_bits", 2, 1 << 33), ("tk_fill_f32", 4, 1 << 32),
           ("tk_fill_f64", 8, 1 << 31), ("tk_fill_bool", 1, 1 << 37), ("tk_fill_normal_f64", 8, 1 << 31),
           ("tk_fill_normal_f32", 4, 1 << 32), ("tk_fill_exponential_f64", 8, 1 << 31),
-          ("tk_fill_exponential_f32", 4, 1 << 32)]
+          ("tk_fill_exponential_f32", 4, 1 << 32), ("tk_fill_normal_f32_half_turn", 4, 1 << 32),
+          ("tk_fill_randn_f32", 4, 1 << 31)]
 
 
 @pytest.mark.parametrize("name,size,limit", SIMPLE)
@@ -108,6 +109,23 @@ def test_philox_validation():
     assert L.tk_philox_fill_u32(1, (1 << 64) - 1, 2, FAKE, None) == tk.TK_ERANGE
     assert L.tk_philox_fill_u64(1, 1 << 63, 1, FAKE, None) == tk.TK_ERANGE
     assert L.tk_philox_fill_f64(1, 0, 4, FAKE + 4, None) == tk.TK_EINVAL
+
+
+def test_philox_variant_validation():
+    top = (1 << 64) - 1
+    assert L.tk_philox_fill_u32_below(1, 0, 4, 0, FAKE, None) == tk.TK_EINVAL
+    assert L.tk_philox_fill_u32_below(1, 0, 4, 7, None, None) == tk.TK_EINVAL
+    assert L.tk_philox_fill_u32_below(1, top, 2, 7, FAKE, None) == tk.TK_ERANGE
+    assert L.tk_philox_fill_u32_below(1, 0, 0, 0, None, None) == tk.TK_EINVAL  # bound first
+    assert L.tk_philox_fill_u64_below(1, 0, 4, 0, FAKE, None) == tk.TK_EINVAL
+    assert L.tk_philox_fill_u64_below(1, 1 << 63, 1, 5, FAKE, None) == tk.TK_ERANGE
+    assert L.tk_philox_fill_u64_below(1, 0, 4, 5, FAKE + 4, None) == tk.TK_EINVAL
+    assert L.tk_philox_fill_normal_f32(1, top, 2, FAKE, None) == tk.TK_ERANGE
+    assert L.tk_philox_fill_normal_f32(1, 0, 4, FAKE + 2, None) == tk.TK_EINVAL
+    assert L.tk_philox_fill_normal_f64(1, 1 << 63, 1, FAKE, None) == tk.TK_ERANGE
+    assert L.tk_philox_fill_normal_f64(1, 0, 1 << 32, FAKE, None) == tk.TK_EINVAL  # n per call
+    assert L.tk_philox_fill_normal_f64(1, 0, 0, None, None) == tk.TK_OK
+    assert L.tk_philox_fill_choice_u32(1, 0, 4, None, FAKE, None) == tk.TK_EINVAL
 
 
 def test_status_strings():
