@@ -222,18 +222,18 @@ def main():
                 "traffic": round(traffic) if traffic is not None else None,
                 "bytes_per_launch": algo_bytes, "avg_launch_ms": round(d["mean_ms"], 5)}
     # rows beyond the hot path: same protocol, separate loop
+    # (back to back as in the step: an event pair around each launch, one sync at the end)
     nxt = {}
     for name, wbytes, _, _, fn in next_rows:
         for s in range(3):
             fn(s)
-        ms = []
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
         for s in range(K):
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
+            ev[s][0].record()
             fn(s)
-            b.record()
-            b.synchronize()
-            ms.append(a.elapsed_time(b))
+            ev[s][1].record()
+        torch.cuda.synchronize()
+        ms = [a.elapsed_time(b) for a, b in ev]
         med = statistics.median(ms)
         nxt[name] = {"GiB_per_s": round(wbytes / (med / 1e3) / GIB, 1), "median_ms": round(med, 4),
                      "median_us": round(med * 1e3, 1)}

@@ -57,14 +57,14 @@ __device__ __forceinline__ uint32_t nibble_to_bytes(uint32_t bits, int shift) {
 // ---- cross-lane hand-off ----------------------------------------------------------------
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63u); }
 
-// The value held by the next lane of the wave (lane 63 receives lane 0's; callers replace
-// it).  Every lane of the wave must execute this.
+// The value held by the next lane of the wave (lane 63 receives 0; callers replace it or
+// do not use it).  A wave-wide DPP shift (wave_shl:1, a gfx9-family VALU move) rather than
+// ds_bpermute, which goes through LDS and costs a wait.  Every lane of the wave must
+// execute this.
 __device__ __forceinline__ uint32_t from_next_lane(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_ds_bpermute((lane_id() + 1) << 2, (int)v);
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x130 /* wave_shl:1 */, 0xF, 0xF, false);
 }
-__device__ __forceinline__ float from_next_lane(float v) {
-  return __int_as_float(__builtin_amdgcn_ds_bpermute((lane_id() + 1) << 2, __float_as_int(v)));
-}
+__device__ __forceinline__ float from_next_lane(float v) { return __uint_as_float(from_next_lane(__float_as_uint(v))); }
 
 // ---- substreams (tandem-sycl, "Design", §Normals: split(g) of sub(PURPOSE) of the key) --
 // The host passes hkp = lowbias32(sub(key, P)); the substream of draw g has key
@@ -214,13 +214,15 @@ __device__ __forceinline__ uint64_t lemire64_sub(uint64_t x, uint64_t s, uint64_
 // Four consecutive Philox words starting at word w0 (word offset w0 & 3 uniform across the
 // launch, and the next lane's w0 four words on): the lane's own block plus, at unaligned
 // offsets, the head of the next lane's.  Every lane of the wave must call this.
-__device__ __forceinline__ uint4 philox_words(uint64_t w0, uint32_t k0, uint32_t k1) {
+// With `overlap` the caller's lane 63 only feeds lane 62 (its own vector is the next wave's
+// first), so it does not compute the next block.
+__device__ __forceinline__ uint4 philox_words(uint64_t w0, uint32_t k0, uint32_t k1, bool overlap = false) {
   const uint64_t b = w0 >> 2;
   const uint32_t o = (uint32_t)(w0 & 3u);
   U32x4 B = philox4x32_10(b, k0, k1);
   if (o == 0) return make_uint4(B.a, B.b, B.c, B.d);
   uint32_t n0 = from_next_lane(B.a), n1 = from_next_lane(B.b), n2 = from_next_lane(B.c);
-  if (lane_id() == 63) {
+  if (!overlap && lane_id() == 63) {
     U32x4 N = philox4x32_10(b + 1, k0, k1);
     n0 = N.a; n1 = N.b; n2 = N.c;
   }
