@@ -113,6 +113,10 @@ def _buf(x, itemsize, n, where):
         return x
     if not x.is_cuda:
         raise ValueError(f"{where}: buffer must live on a HIP device")
+    import torch
+    if x.device.index != torch.cuda.current_device():
+        # the library launches on the calling thread's current device
+        raise ValueError(f"{where}: buffer is on {x.device}, the current device is cuda:{torch.cuda.current_device()}")
     if x.element_size() != itemsize:
         raise ValueError(f"{where}: element size {x.element_size()} != {itemsize}")
     if not x.is_contiguous() or x.numel() < n:

@@ -156,3 +156,12 @@ def test_alias_host_build_is_the_oracles(weights):
     q, a = tk.tk_alias_build_host(weights)
     qo, ao, _ = oracle.alias_build(weights)
     assert np.array_equal(q, qo) and np.array_equal(a, ao)
+
+
+def test_binding_refuses_host_tensors_and_bad_buffers():
+    """The binding passes device buffers only; host tensors are refused before any call."""
+    import torch
+    with pytest.raises(ValueError, match="HIP device"):
+        tk.tk_fill_u32(1, 0, 4, torch.empty(4, dtype=torch.int32))
+    with pytest.raises(ValueError, match="HIP device"):
+        tk.tk_dropout_f32(1, 0, 4, 0.1, torch.empty(4), torch.empty(4))
