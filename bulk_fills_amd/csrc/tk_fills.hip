@@ -349,16 +349,16 @@ struct OpRandnF32 : FillBase<float> {
 // f64: u = (d & (2^53 - 1)) 2^-53 of the 64-bit draw.
 struct OpExpF64 : FillBase<uint64_t> {
   uint32_t hk;
-  __device__ __forceinline__ uint64_t one(uint32_t lo, uint32_t hi) const {
-    return (uint64_t)__double_as_longlong(neg_ln_unit(1.0 - unit53_lowbits(lo, hi)));
+  __device__ __forceinline__ uint64_t one(uint32_t lo, uint32_t hi, const LogEntry *tab) const {
+    return (uint64_t)__double_as_longlong(neg_ln_unit(1.0 - unit53_lowbits(lo, hi), tab));
   }
   __device__ __forceinline__ uint64_t elem(uint64_t k) const {
     const uint32_t c = 2u * (uint32_t)(start + k);
-    return one(word(hk, c), word(hk, c + 1));
+    return one(word(hk, c), word(hk, c + 1), kLogTable);
   }
-  __device__ __forceinline__ uint4 vec(uint64_t v) const {
+  __device__ __forceinline__ uint4 vec(uint64_t v, const LogEntry *tab) const {
     const uint32_t c = 2u * (uint32_t)vec_draw(v);
-    const uint64_t a = one(word(hk, c), word(hk, c + 1)), b = one(word(hk, c + 2), word(hk, c + 3));
+    const uint64_t a = one(word(hk, c), word(hk, c + 1), tab), b = one(word(hk, c + 2), word(hk, c + 3), tab);
     return u4(lo32(a), hi32(a), lo32(b), hi32(b));
   }
 };
@@ -366,15 +366,57 @@ struct OpExpF64 : FillBase<uint64_t> {
 // f32: u = (w & 0xFFFFFF) 2^-24.
 struct OpExpF32 : FillBase<uint32_t> {
   uint32_t hk;
-  __device__ __forceinline__ uint32_t one(uint32_t w) const {
-    return __float_as_uint((float)neg_ln_unit(1.0 - (double)(w & 0xFFFFFFu) * 0x1p-24));
+  __device__ __forceinline__ uint32_t one(uint32_t w, const LogEntry *tab) const {
+    return __float_as_uint((float)neg_ln_unit(1.0 - (double)(w & 0xFFFFFFu) * 0x1p-24, tab));
   }
-  __device__ __forceinline__ uint32_t elem(uint64_t k) const { return one(word(hk, (uint32_t)(start + k))); }
-  __device__ __forceinline__ uint4 vec(uint64_t v) const {
+  __device__ __forceinline__ uint32_t elem(uint64_t k) const { return one(word(hk, (uint32_t)(start + k)), kLogTable); }
+  __device__ __forceinline__ uint4 vec(uint64_t v, const LogEntry *tab) const {
     const uint32_t c = (uint32_t)vec_draw(v);
-    return u4(one(word(hk, c)), one(word(hk, c + 1)), one(word(hk, c + 2)), one(word(hk, c + 3)));
+    return u4(one(word(hk, c), tab), one(word(hk, c + 1), tab), one(word(hk, c + 2), tab), one(word(hk, c + 3), tab));
   }
 };
+
+// Exponential fills: T 4 KiB tiles per work-group after copying the 4 KiB logarithm table
+// to LDS (one 16-byte load per thread), so the per-element table reads are ds_reads and
+// not L1 gathers through the texture addresser.
+template <class Op, int T, bool kNT>
+__global__ __launch_bounds__(kBlock) void k_exp_fill(Op op) {
+  static_assert(sizeof(LogEntry) * TK_LOG_ENTRIES == 16 * kBlock, "one 16-byte piece of the table per thread");
+  __shared__ LogEntry tab[TK_LOG_ENTRIES];
+  ((uint4 *)tab)[threadIdx.x] = ((const uint4 *)kLogTable)[threadIdx.x];
+  __syncthreads();
+  const uint64_t v0 = (uint64_t)blockIdx.x * T * kBlock + threadIdx.x;
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    const uint64_t v = v0 + (uint64_t)t * kBlock;
+    const uint4 r = op.vec(v, tab);
+    if (v < op.nvec) store16<kNT>(op.vec_ptr(v), r);
+  }
+  if (blockIdx.x == 0) write_edges(op);
+}
+
+template <class Op, int T>
+static tk_status launch_exp_t(const Op &op, hipStream_t stream) {
+  const uint64_t per = (uint64_t)kBlock * T;
+  uint64_t grid = (op.nvec + per - 1) / per;
+  if (grid == 0) grid = 1;
+  if (grid > 0x7FFFFFFFull) return TK_EINVAL;
+  if (config().nt_stores)
+    hipLaunchKernelGGL((k_exp_fill<Op, T, true>), dim3((uint32_t)grid), dim3(kBlock), 0, stream, op);
+  else
+    hipLaunchKernelGGL((k_exp_fill<Op, T, false>), dim3((uint32_t)grid), dim3(kBlock), 0, stream, op);
+  return launch_status();
+}
+
+template <class Op, class T>
+static tk_status run_exp(Op op, T *out, uint64_t start, uint64_t n, hipStream_t stream) {
+  set_geometry(op, out, start, n);
+  switch (config().exp_tiles) {
+    case 1: return launch_exp_t<Op, 1>(op, stream);
+    case 4: return launch_exp_t<Op, 4>(op, stream);
+    default: return launch_exp_t<Op, 2>(op, stream);
+  }
+}
 
 // ---------------------------------------------------------------------------------------
 // Fused dropout: y = u >= p ? x / (1 - p) : +0 (IEEE f32 division), optional mask bytes
@@ -719,14 +761,14 @@ tk_status tk_fill_exponential_f64(uint32_t key, uint64_t start_draw, uint64_t n,
   TK_PRECHECK(out, kMaxW64);
   OpExpF64 op{};
   op.hk = host_lowbias32(key);
-  return run_simple(op, (uint64_t *)out, start_draw, n, stream);
+  return run_exp(op, (uint64_t *)out, start_draw, n, stream);
 }
 
 tk_status tk_fill_exponential_f32(uint32_t key, uint64_t start_draw, uint64_t n, float *out, hipStream_t stream) {
   TK_PRECHECK(out, kMaxW32);
   OpExpF32 op{};
   op.hk = host_lowbias32(key);
-  return run_simple(op, (uint32_t *)out, start_draw, n, stream);
+  return run_exp(op, (uint32_t *)out, start_draw, n, stream);
 }
 
 tk_status tk_dropout_f32(uint32_t key, uint64_t start_draw, uint64_t n, float p, const float *x, float *y,

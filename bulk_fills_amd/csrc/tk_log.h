@@ -10,6 +10,8 @@
 // points of the 2^-24 grid and 2^26 random points of the 2^-53 grid the error is at most
 // 0.514 ulp, and rounding it to f32 gives the correctly rounded f32 at every grid point.
 // About 30 VALU operations and two 16-byte table reads; the compiler's log takes ~115.
+// The fills read the table from an LDS copy per work-group: as L1 gathers the reads kept
+// the texture addresser ~95 % busy (rocprofv3 TA_TA_BUSY) and bounded both fills.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -25,15 +27,16 @@ struct LogEntry {
 
 static __constant__ LogEntry kLogTable[TK_LOG_ENTRIES] = {TK_LOG_TABLE_ROWS};
 
-// -ln x for x in [2^-53, 1] (every 1 - u of the fills); exactly +0 at x = 1.
-__device__ __forceinline__ double neg_ln_unit(double x) {
+// -ln x for x in [2^-53, 1] (every 1 - u of the fills); exactly +0 at x = 1.  `tab` is
+// kLogTable or a work-group's LDS copy of it.
+__device__ __forceinline__ double neg_ln_unit(double x, const LogEntry *tab) {
   const uint32_t xh = (uint32_t)__double2hiint(x);
   const uint32_t j = (xh >> 13) & (TK_LOG_ENTRIES - 1);  // 7 leading fraction bits
   const bool half = j >= TK_LOG_SPLIT;
   const int32_t n = 1023 - (int32_t)(xh >> 20) - (half ? 1 : 0);  // -E, 0 <= n <= 53
   const uint32_t zh = (xh & 0x000FFFFFu) | (half ? 0x3FE00000u : 0x3FF00000u);
   const double z = __hiloint2double((int)zh, __double2loint(x));
-  const LogEntry t = kLogTable[j];
+  const LogEntry t = tab[j];
   const double f = z - t.c;                                   // exact
   const double qh = f * t.invc;
   const double ql = __builtin_fma(-qh, t.c, f) * t.invc;      // the residual is exact
