@@ -115,37 +115,41 @@ __device__ __forceinline__ void zig_primary(const ZigArgs &a, uint64_t k, uint32
   }
 }
 
-// Stores entry k at position `slot` of the work-group's queue if below `cap`.  Past it, a
-// fused table pass only counts the miss (the group re-walks); the two-kernel pass appends
-// it to the overflow list.
+// The work-group's miss queue is one region per wave, so a wave appends without atomics:
+// it counts its misses in a wave-uniform register and ranks them with ballots.  `q` is
+// the wave's region, `cap` its usable entries.  Past `cap`, a fused table pass only
+// counts the miss (the group re-walks); the two-kernel pass appends it to the overflow
+// list.
+struct WaveQueue {
+  uint32_t *q;
+  uint32_t cap;
+  uint32_t n;  // misses seen (wave-uniform)
+};
+
 template <bool kFused>
-__device__ __forceinline__ void queue_put(uint32_t slot, uint32_t k, uint32_t *q, uint32_t cap, const ZigArgs &a) {
-  if (slot < cap) {
-    q[slot] = k;
+__device__ __forceinline__ void queue_put(uint32_t slot, uint32_t k, const WaveQueue &wq, const ZigArgs &a) {
+  if (slot < wq.cap) {
+    wq.q[slot] = k;
   } else if (!kFused) {
     const uint32_t g = atomicAdd(&a.ctr[0], 1u);
     if (g < a.ovf_cap) a.ovf[g] = k;
   }
 }
 
-// Appends the lane's misses (element k0 when p0, k0 + 1 when p1) to the work-group's
-// queue: two ballots, one LDS atomic per wave, ranks from mbcnt.  Called by all lanes of
-// the wave (every lane is active in the table pass).
+__device__ __forceinline__ uint32_t lane_rank(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+// Appends the lane's misses (element k0 when p0, k0 + 1 when p1) to the wave's region:
+// two ballots, ranks from mbcnt.  Called by all lanes of the wave.
 template <bool kFused>
-__device__ __forceinline__ void enqueue2(bool p0, bool p1, uint32_t k0, uint32_t *q, uint32_t *qn, uint32_t cap,
-                                         const ZigArgs &a) {
+__device__ __forceinline__ void enqueue2(bool p0, bool p1, uint32_t k0, WaveQueue &wq, const ZigArgs &a) {
   const uint64_t m0 = __builtin_amdgcn_ballot_w64(p0), m1 = __builtin_amdgcn_ballot_w64(p1);
   if ((m0 | m1) == 0) return;
   const uint32_t c0 = (uint32_t)__popcll(m0);
-  uint32_t base = 0;
-  if (lane_id() == 0) base = atomicAdd(qn, c0 + (uint32_t)__popcll(m1));
-  base = (uint32_t)__shfl((int)base, 0);
-  if (p0)
-    queue_put<kFused>(base + __builtin_amdgcn_mbcnt_hi((uint32_t)(m0 >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m0, 0u)),
-                      k0, q, cap, a);
-  if (p1)
-    queue_put<kFused>(base + c0 + __builtin_amdgcn_mbcnt_hi((uint32_t)(m1 >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m1, 0u)),
-                      k0 + 1, q, cap, a);
+  if (p0) queue_put<kFused>(wq.n + lane_rank(m0), k0, wq, a);
+  if (p1) queue_put<kFused>(wq.n + c0 + lane_rank(m1), k0 + 1, wq, a);
+  wq.n += c0 + (uint32_t)__popcll(m1);
 }
 
 template <bool kPhilox>
@@ -153,71 +157,33 @@ __device__ double zig_slow(const ZigArgs &a, uint64_t k);
 
 // Table pass: T consecutive 4 KiB tiles per work-group.  With kLds the 16 KiB layer table
 // is first copied to LDS (one copy per T tiles) and gathered from there; otherwise the
-// gathers go to the table in device memory through L1/L2.
+// gathers go to the table in device memory through L1/L2.  Misses go to the queue region
+// of their wave (4T entries, about 2.2 expected at T = 4), appended without atomics.
 // With kFused the work-group finishes its own misses after its stores, while the lines it
-// just wrote are still in L2.  Its queue holds 16 misses per tile (about 2.2 expected); a
-// group that finds more (probability ~1e-10) walks its own elements again and finishes
-// every miss it meets, so nothing leaves the work-group.  Otherwise the queue goes to the
-// group's slot for the continuation pass.
-// One tile: 256 lanes, two elements each.  kCheck guards vectors past the end (only the
-// last group needs it).
-template <bool kAligned4, bool kCheck, bool kFused, bool kNT, bool kPhilox>
-__device__ __forceinline__ void zig_tile(const ZigArgs &a, const double2 *tab, uint64_t v, uint32_t *q,
-                                         uint32_t *qn, uint32_t cap) {
-  const bool in = !kCheck || v < a.nvec;
-  uint32_t w[4];
-  zig_words<kAligned4, kPhilox>(a, v, w);
-  double y0, y1;
-  const bool f0 = zig_fast(tab, w[0], w[1], &y0);
-  const bool f1 = zig_fast(tab, w[2], w[3], &y1);
-  if (in) {
-    uint4 o;
-    o.x = (uint32_t)__double_as_longlong(y0);
-    o.y = (uint32_t)((uint64_t)__double_as_longlong(y0) >> 32);
-    o.z = (uint32_t)__double_as_longlong(y1);
-    o.w = (uint32_t)((uint64_t)__double_as_longlong(y1) >> 32);
-    store16<kNT>(a.out + a.head + 2 * v, o);
-  }
-  enqueue2<kFused>(in && !f0, in && !f1, (uint32_t)(a.head + 2 * v), q, qn, cap, a);
-}
-
-template <int T, bool kAligned4, bool kFused, bool kNT, bool kPhilox>
-__device__ __forceinline__ void zig_tiles(const ZigArgs &a, const double2 *tab, uint32_t *q, uint32_t *qn,
-                                          uint32_t cap) {
-  const uint64_t v0 = (uint64_t)blockIdx.x * T * kBlock + threadIdx.x;
-  if ((uint64_t)(blockIdx.x + 1) * T * kBlock <= a.nvec) {
-    for (int t = 0; t < T; ++t)
-      zig_tile<kAligned4, false, kFused, kNT, kPhilox>(a, tab, v0 + (uint64_t)t * kBlock, q, qn, cap);
-  } else {
-    for (int t = 0; t < T; ++t)
-      zig_tile<kAligned4, true, kFused, kNT, kPhilox>(a, tab, v0 + (uint64_t)t * kBlock, q, qn, cap);
-  }
-}
-
-// Table pass: T consecutive 4 KiB tiles per work-group.  With kLds the 16 KiB layer table
-// is first copied to LDS (one copy per T tiles) and gathered from there; otherwise the
-// gathers go to the table in device memory through L1/L2.
-// With kFused the work-group finishes its own misses after its stores, while the lines it
-// just wrote are still in L2.  Its queue holds 16 misses per tile (about 2.2 expected); a
-// group that finds more (probability ~1e-10) walks its own elements again and finishes
-// every miss it meets, so nothing leaves the work-group.  Otherwise the queue goes to the
-// group's slot for the continuation pass.
+// just wrote are still in L2; a group with a wave that found more misses than its region
+// holds (probability ~1e-10 per wave) walks its own elements again and finishes every miss
+// it meets, so nothing leaves the work-group.  Otherwise the queue goes to the group's
+// slot for the continuation pass.
 template <int T, bool kLds, bool kNT, bool kFused, bool kPhilox>
 __global__ __launch_bounds__(kBlock) void k_zig_table_pass(ZigArgs a) {
-  constexpr uint32_t kQueue = kSlotPerTile * T + (kFused ? 2u : 0u);  // fused: + block 0's edge elements
+  constexpr uint32_t kWaves = kBlock / 64;
+  constexpr uint32_t kPerWave = kSlotPerTile * T / kWaves;  // a wave's share of the group's slot
+  constexpr uint32_t kRegion = kPerWave + (kFused ? 1u : 0u);  // fused: + an edge element (waves 0 and 1)
   __shared__ double2 lds_tab[kLds ? 1024 : 1];
-  __shared__ uint32_t q[kQueue];
-  __shared__ uint32_t qn;
-  if (kLds)
+  __shared__ uint32_t q[kWaves * kRegion];
+  __shared__ uint32_t wave_n[kWaves];
+  if (kLds) {
     for (uint32_t i = threadIdx.x; i < 1024; i += kBlock) lds_tab[i] = a.xx[i];
-  if (threadIdx.x == 0) qn = 0;
-  __syncthreads();
-  // fused: entries past `cap` are only counted (the group re-walks); two kernels: they go
-  // to the overflow list
-  const uint32_t cap = kFused ? (a.slot_cap < kQueue ? a.slot_cap : kQueue) : a.slot_cap;
+    __syncthreads();
+  }
+  const uint32_t w = threadIdx.x >> 6;
+  // entries a wave keeps: its share of the group's slot capacity (smaller when a test
+  // shrinks the slots), plus the edge element in the fused pass
+  const uint32_t share = (a.slot_cap + kWaves - 1) / kWaves;
+  WaveQueue wq{q + w * kRegion, (share < kPerWave ? share : kPerWave) + (kFused ? 1u : 0u), 0u};
   const double2 *tab = kLds ? lds_tab : a.xx;
-  if (((a.start + a.head) & 1u) == 0) zig_tiles<T, true, kFused, kNT, kPhilox>(a, tab, q, &qn, cap);
-  else zig_tiles<T, false, kFused, kNT, kPhilox>(a, tab, q, &qn, cap);
+  if (((a.start + a.head) & 1u) == 0) zig_tiles<T, true, kFused, kNT, kPhilox>(a, tab, wq);
+  else zig_tiles<T, false, kFused, kNT, kPhilox>(a, tab, wq);
   if (blockIdx.x == 0) {  // the element before the first boundary and the one after the last vector
     const uint32_t t = threadIdx.x;
     bool edge = false;
@@ -232,18 +198,35 @@ __global__ __launch_bounds__(kBlock) void k_zig_table_pass(ZigArgs a) {
       fast = zig_fast(tab, lo, hi, &y);
       a.out[k] = y;
     }
-    enqueue2<kFused>(edge && !fast, false, (uint32_t)k, q, &qn, cap, a);
+    enqueue2<kFused>(edge && !fast, false, (uint32_t)k, wq, a);
   }
+  if (lane_id() == 0) wave_n[w] = wq.n;
   __syncthreads();
-  const uint32_t total = qn;
+  // the kept entries of all regions, numbered in wave order
+  uint32_t seen = 0, kept = 0, off[kWaves];
+  bool over = false;
+#pragma unroll
+  for (uint32_t i = 0; i < kWaves; ++i) {
+    const uint32_t ni = wave_n[i];
+    seen += ni;
+    over |= ni > wq.cap;
+    off[i] = kept;
+    kept += ni < wq.cap ? ni : wq.cap;
+  }
+  auto entry = [&](uint32_t j) {  // j < kept
+    uint32_t i = 0;
+#pragma unroll
+    for (uint32_t r = 1; r < kWaves; ++r) i += j >= off[r] ? 1u : 0u;
+    return q[i * kRegion + (j - off[i])];
+  };
   if (kFused) {
-    if (threadIdx.x == 0) a.counts[blockIdx.x] = total;
-    if (total <= cap) {
-      for (uint32_t j = threadIdx.x; j < total; j += kBlock) {
-        const uint32_t k = q[j];
+    if (threadIdx.x == 0) a.counts[blockIdx.x] = seen;
+    if (!over) {
+      for (uint32_t j = threadIdx.x; j < kept; j += kBlock) {
+        const uint32_t k = entry(j);
         a.out[k] = zig_slow<kPhilox>(a, k);
       }
-    } else {  // more misses than the queue holds: walk the group's elements again
+    } else {  // a wave had more misses than its region holds: walk the group's elements again
       const uint64_t e0 = a.head + (uint64_t)blockIdx.x * T * kBlock * 2;
       uint64_t e1 = e0 + (uint64_t)T * kBlock * 2;
       if (e1 > a.head + 2 * a.nvec) e1 = a.head + 2 * a.nvec;
@@ -264,10 +247,9 @@ __global__ __launch_bounds__(kBlock) void k_zig_table_pass(ZigArgs a) {
         }
       }
     }
-  } else {
-    const uint32_t nq = total < a.slot_cap ? total : a.slot_cap;
-    if (threadIdx.x == 0) a.counts[blockIdx.x] = nq;
-    for (uint32_t i = threadIdx.x; i < nq; i += kBlock) a.slots[(uint64_t)blockIdx.x * a.slot_size + i] = q[i];
+  } else {  // the kept entries go to the group's slot (at most kWaves * kPerWave = slot_size)
+    if (threadIdx.x == 0) a.counts[blockIdx.x] = kept;
+    for (uint32_t j = threadIdx.x; j < kept; j += kBlock) a.slots[(uint64_t)blockIdx.x * a.slot_size + j] = entry(j);
   }
 }
 
