@@ -155,6 +155,40 @@ __device__ __forceinline__ void enqueue2(bool p0, bool p1, uint32_t k0, WaveQueu
 template <bool kPhilox>
 __device__ double zig_slow(const ZigArgs &a, uint64_t k);
 
+// One tile: 256 lanes, two elements each.  kCheck guards vectors past the end (only the
+// last group needs it).
+template <bool kAligned4, bool kCheck, bool kFused, bool kNT, bool kPhilox>
+__device__ __forceinline__ void zig_tile(const ZigArgs &a, const double2 *tab, uint64_t v, WaveQueue &wq) {
+  const bool in = !kCheck || v < a.nvec;
+  uint32_t w[4];
+  zig_words<kAligned4, kPhilox>(a, v, w);
+  double y0, y1;
+  const bool f0 = zig_fast(tab, w[0], w[1], &y0);
+  const bool f1 = zig_fast(tab, w[2], w[3], &y1);
+  if (in) {
+    uint4 o;
+    o.x = (uint32_t)__double_as_longlong(y0);
+    o.y = (uint32_t)((uint64_t)__double_as_longlong(y0) >> 32);
+    o.z = (uint32_t)__double_as_longlong(y1);
+    o.w = (uint32_t)((uint64_t)__double_as_longlong(y1) >> 32);
+    store16<kNT>(a.out + a.head + 2 * v, o);
+  }
+  enqueue2<kFused>(in && !f0, in && !f1, (uint32_t)(a.head + 2 * v), wq, a);
+}
+
+template <int T, bool kAligned4, bool kFused, bool kNT, bool kPhilox>
+__device__ __forceinline__ void zig_tiles(const ZigArgs &a, const double2 *tab, WaveQueue &wq) {
+  const uint64_t v0 = (uint64_t)blockIdx.x * T * kBlock + threadIdx.x;
+  if ((uint64_t)(blockIdx.x + 1) * T * kBlock <= a.nvec) {
+    for (int t = 0; t < T; ++t)
+      zig_tile<kAligned4, false, kFused, kNT, kPhilox>(a, tab, v0 + (uint64_t)t * kBlock, wq);
+  } else {
+    for (int t = 0; t < T; ++t)
+      zig_tile<kAligned4, true, kFused, kNT, kPhilox>(a, tab, v0 + (uint64_t)t * kBlock, wq);
+  }
+}
+
+
 // Table pass: T consecutive 4 KiB tiles per work-group.  With kLds the 16 KiB layer table
 // is first copied to LDS (one copy per T tiles) and gathered from there; otherwise the
 // gathers go to the table in device memory through L1/L2.  Misses go to the queue region
