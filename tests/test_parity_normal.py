@@ -172,3 +172,38 @@ def test_f32_full_2p28_sampled():
     for s in tk_inputs.STARTS:
         tk.tk_fill_normal_f32(1, s, n, b.ptr)
         assert f32_err(b.sample(idx, np.float32), 1, 0, draws=idx.astype(np.uint64) + s) <= F32_ABS
+
+
+def test_host_threads_share_the_device_state():
+    """Any host thread may call (include/tk.h): four threads, each with its own stream,
+    fill normals and exponentials at once (ctypes releases the GIL during the calls), so
+    calls race on the per-device ziggurat state's mutex and event; every result must equal
+    the oracle's."""
+    import threading
+    n = (1 << 19) + 5
+    keys = [21, 22, 23, 24]
+    bufs = {k: (DevBuf(n, 8), DevBuf(n, 4)) for k in keys}
+    errors = []
+    torch.cuda.synchronize()
+
+    def work(key):
+        try:
+            s = torch.cuda.Stream()
+            for rep in range(6):
+                tk.tk_fill_normal_f64(key, rep, n, bufs[key][0].ptr, stream=s)
+                tk.tk_fill_exponential_f32(key, rep, n, bufs[key][1].ptr, stream=s)
+            s.synchronize()
+        except Exception as e:  # reported after the join
+            errors.append(repr(e))
+
+    threads = [threading.Thread(target=work, args=(k,)) for k in keys]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for k in keys:
+        check_f64(bufs[k][0].host(np.float64), k, 5, n, what=f"thread key {k}")
+        got = bufs[k][1].host(np.float32)
+        assert np.array_equal(got.view(np.uint32), oracle.fill_exponential_f32(k, 5, n).view(np.uint32)), k
