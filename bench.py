@@ -33,7 +33,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--warmup-seconds", type=float, default=2.0,
                     help="keep warming up for at least this long (the pages warm each row for 2 s)")
-    ap.add_argument("--cpu-sample-log2", type=int, default=26,
+    ap.add_argument("--cpu-sample-log2", type=int, default=27,
                     help="elements per fill in the oracle's CPU sample (0 disables it)")
     ap.add_argument("--only", default="",
                     help="comma-separated fill names to run (profiling); 'calib_copy' adds a plain 1 GiB "
