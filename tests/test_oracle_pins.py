@@ -601,7 +601,8 @@ def test_choice_matches_exact_probabilities():
 
 
 # ---------------------------------------------------------------------------------------
-# Philox4x32-10: parity unpinned (no known-answer vectors here); layout and statistics only
+# Philox4x32-10: parity unpinned (no known-answer vectors here); layout, statistics and
+# inversion of the rounds only
 # ---------------------------------------------------------------------------------------
 
 def test_philox_layout_and_statistics():
@@ -616,6 +617,45 @@ def test_philox_layout_and_statistics():
     hi = oracle.philox_fill_u32(1, 4 << 32, 4)
     lo = oracle.philox_fill_u32(1, 0, 4)
     assert not np.array_equal(hi, lo)
+
+
+def _philox_unround(y, a, b):
+    """Undoes one Philox4x32 round under round key (a, b) (Salmon et al., SC'11, section 5:
+    the round is a bijection because the multipliers are odd).  The low halves of the two
+    products are output lanes 1 and 3, so the multiplied inputs come back through the
+    multipliers' inverses mod 2^32; the high halves then strip off lanes 0 and 2."""
+    m0, m1 = 0xD2511F53, 0xCD9E8D57
+    x2 = (y[1] * pow(m1, -1, 1 << 32)) & 0xFFFFFFFF
+    x0 = (y[3] * pow(m0, -1, 1 << 32)) & 0xFFFFFFFF
+    x1 = y[0] ^ ((m1 * x2) >> 32) ^ a
+    x3 = y[2] ^ ((m0 * x0) >> 32) ^ b
+    return [x0, x1, x2, x3]
+
+
+def _philox_invert(block, key, rounds=10):
+    k0, k1 = key & 0xFFFFFFFF, key >> 32
+    y = list(block)
+    for r in reversed(range(rounds)):
+        y = _philox_unround(y, (k0 + r * 0x9E3779B9) & 0xFFFFFFFF, (k1 + r * 0xBB67AE85) & 0xFFFFFFFF)
+    return y
+
+
+def test_philox_blocks_invert_to_their_counters():
+    """Structure pin: running ten inverse rounds (each undone from the round's definition,
+    not by re-running it) over the oracle's block must give back the counter it was asked
+    for, for counters in all four lanes.  A slip in the lane order, the hi/lo halves, the
+    key words or the key schedule would not invert.  The constants themselves and the
+    output order stay unpinned against a third party."""
+    rng = np.random.default_rng(7)
+    for key in (0, 1, 0xFFFFFFFFFFFFFFFF, 0x0123456789ABCDEF, int(rng.integers(0, 1 << 63))):
+        for b in (0, 1, (1 << 32) + 5, (1 << 62) - 1):  # primary blocks: counter (lo32 b, hi32 b, 0, 0)
+            blk = [int(v) for v in oracle.philox_fill_u32(key, 4 * b, 4)]
+            assert _philox_invert(blk, key) == [b & 0xFFFFFFFF, b >> 32, 0, 0]
+        for _ in range(50):  # substream blocks: counter (lo32 i, hi32 i, P, j >> 2)
+            i, pur, jb = int(rng.integers(0, 1 << 63)), int(rng.integers(0, 1 << 32)), int(rng.integers(0, 1 << 28))
+            blk = [int(oracle.philox_sub_word(key, i, pur, 4 * jb + lane)) for lane in range(4)]
+            assert _philox_invert(blk, key) == [i & 0xFFFFFFFF, i >> 32, pur, jb]
+            assert _philox_invert(blk, key, rounds=9) != [i & 0xFFFFFFFF, i >> 32, pur, jb]
 
 
 # ---------------------------------------------------------------------------------------
