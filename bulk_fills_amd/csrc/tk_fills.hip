@@ -133,6 +133,20 @@ static tk_status launch_vec(const Op &op, hipStream_t stream) {
   return launch_status();
 }
 
+// The same launch with non-temporal 16-byte stores whatever TK_STORE says: for dropout,
+// whose input is read with non-temporal loads.  A 1 GiB scaled copy measured 6.2 TB/s moved
+// with plain loads and stores, 6.5 with non-temporal loads and 6.6 with both; the 2^28
+// dropout went from ~346 to ~328 us (out of place) and from ~358 to ~324 us (in place).
+template <class Op>
+static tk_status launch_vec_nt(const Op &op, hipStream_t stream) {
+  uint64_t ntiles = (op.nvec + kBlock - 1) / kBlock;
+  uint64_t grid = ntiles ? ntiles : 1;
+  if (grid > config().max_blocks) grid = config().max_blocks;
+  if (grid > 0x7FFFFFFFull) grid = 0x7FFFFFFFull;
+  hipLaunchKernelGGL((k_vec_fill<Op, 1, true>), dim3((uint32_t)grid), dim3(kBlock), 0, stream, op, ntiles);
+  return launch_status();
+}
+
 __device__ __forceinline__ uint4 u4(uint32_t a, uint32_t b, uint32_t c, uint32_t d) { return make_uint4(a, b, c, d); }
 __device__ __forceinline__ uint32_t lo32(uint64_t x) { return (uint32_t)x; }
 __device__ __forceinline__ uint32_t hi32(uint64_t x) { return (uint32_t)(x >> 32); }
@@ -437,8 +451,9 @@ struct OpDropout : FillBase<float> {
     if (v >= nvec) return u4(0, 0, 0, 0);  // never read x past the end
     const uint64_t k0 = head + 4 * v;
     float xv[4];
-    if (x_vec) {
-      float4 t = *(const float4 *)(x + k0);
+    if (x_vec) {  // x is read once: a non-temporal load (streams past the caches)
+      typedef float f32x4 __attribute__((ext_vector_type(4)));
+      const f32x4 t = __builtin_nontemporal_load((const f32x4 *)(x + k0));
       xv[0] = t.x; xv[1] = t.y; xv[2] = t.z; xv[3] = t.w;
     } else {
 #pragma unroll
@@ -791,7 +806,7 @@ tk_status tk_dropout_f32(uint32_t key, uint64_t start_draw, uint64_t n, float p,
   op.q = 1.0f - p;
   op.x_vec = (((uintptr_t)(x + op.head)) & 15u) == 0;
   op.mask_word = mask && (((uintptr_t)(mask + op.head)) & 3u) == 0;
-  return launch_vec(op, stream);
+  return launch_vec_nt(op, stream);
 }
 
 tk_status tk_dropout_backward_f32(uint32_t key, uint64_t start_draw, uint64_t n, float p, const float *dy,

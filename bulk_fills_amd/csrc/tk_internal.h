@@ -46,7 +46,7 @@ struct Config {
   int unroll;               // TK_UNROLL: 16-byte vectors per lane per tile (1, 2 or 4)
   int choice_tiles;         // TK_CHOICE_TILES: 4 KiB tiles per choice work-group (1, 2, 4, 8)
   int exp_tiles;            // TK_EXP_TILES: 4 KiB tiles per exponential work-group (1, 2, 4)
-  int zig_tiles;            // TK_ZIG_TILES: 4 KiB tiles per ziggurat table-pass work-group (1 or 8)
+  int zig_tiles;            // TK_ZIG_TILES: tiles (one 16-byte vector per lane) per table-pass work-group
   bool zig_fused;           // TK_ZIG_MODE=fused|split: misses finished in the table pass, or in a second kernel
   bool zig_lds;             // TK_ZIG_TABLE=lds|global: where the table pass gathers the layers
 };

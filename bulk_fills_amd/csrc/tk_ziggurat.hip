@@ -37,6 +37,13 @@ namespace tk {
 
 constexpr uint32_t kSlotPerTile = 16;  // miss entries a work-group keeps per 4 KiB tile
 
+// Miss-queue entries per wave of a table-pass group of kB lanes and T tiles: 4 per tile
+// of 512 elements (2.2 expected misses per 256-lane tile, so 16 per 256-lane tile), and at
+// least 8 (a wave sees Poisson(0.55) misses per tile; more than 8 happens about once in
+// 1e8 waves, and then the group walks its elements again).
+constexpr uint32_t zig_wave_entries(int T) { return 4u * (uint32_t)T > 8u ? 4u * (uint32_t)T : 8u; }
+constexpr uint32_t zig_slot_entries(int kB, int T) { return (uint32_t)(kB / 64) * zig_wave_entries(T); }
+
 struct ZigArgs {
   double *out;
   uint64_t start;  // draw of element 0
@@ -176,38 +183,43 @@ __device__ __forceinline__ void zig_tile(const ZigArgs &a, const double2 *tab, u
   enqueue2<kFused>(in && !f0, in && !f1, (uint32_t)(a.head + 2 * v), wq, a);
 }
 
-template <int T, bool kAligned4, bool kFused, bool kNT, bool kPhilox>
+template <int kB, int T, bool kAligned4, bool kFused, bool kNT, bool kPhilox>
 __device__ __forceinline__ void zig_tiles(const ZigArgs &a, const double2 *tab, WaveQueue &wq) {
-  const uint64_t v0 = (uint64_t)blockIdx.x * T * kBlock + threadIdx.x;
-  if ((uint64_t)(blockIdx.x + 1) * T * kBlock <= a.nvec) {
+  const uint64_t v0 = (uint64_t)blockIdx.x * T * kB + threadIdx.x;
+  if ((uint64_t)(blockIdx.x + 1) * T * kB <= a.nvec) {
     for (int t = 0; t < T; ++t)
-      zig_tile<kAligned4, false, kFused, kNT, kPhilox>(a, tab, v0 + (uint64_t)t * kBlock, wq);
+      zig_tile<kAligned4, false, kFused, kNT, kPhilox>(a, tab, v0 + (uint64_t)t * kB, wq);
   } else {
     for (int t = 0; t < T; ++t)
-      zig_tile<kAligned4, true, kFused, kNT, kPhilox>(a, tab, v0 + (uint64_t)t * kBlock, wq);
+      zig_tile<kAligned4, true, kFused, kNT, kPhilox>(a, tab, v0 + (uint64_t)t * kB, wq);
   }
 }
 
-
-// Table pass: T consecutive 4 KiB tiles per work-group.  With kLds the 16 KiB layer table
-// is first copied to LDS (one copy per T tiles) and gathered from there; otherwise the
-// gathers go to the table in device memory through L1/L2.  Misses go to the queue region
-// of their wave (4T entries, about 2.2 expected at T = 4), appended without atomics.
+// Table pass: T consecutive tiles of kB lanes (one 16-byte vector per lane each) per
+// work-group.  With kLds the 16 KiB layer table is first copied to LDS (one copy per T
+// tiles) and gathered from there; otherwise the gathers go to the table in device memory
+// through L1/L2.  Misses go to the queue region of their wave (zig_wave_entries(T)
+// entries; a wave expects 0.55 misses per tile), appended without atomics.
 // With kFused the work-group finishes its own misses after its stores, while the lines it
 // just wrote are still in L2; a group with a wave that found more misses than its region
 // holds (probability ~1e-10 per wave) walks its own elements again and finishes every miss
 // it meets, so nothing leaves the work-group.  Otherwise the queue goes to the group's
 // slot for the continuation pass.
-template <int T, bool kLds, bool kNT, bool kFused, bool kPhilox>
-__global__ __launch_bounds__(kBlock) void k_zig_table_pass(ZigArgs a) {
-  constexpr uint32_t kWaves = kBlock / 64;
-  constexpr uint32_t kPerWave = kSlotPerTile * T / kWaves;  // a wave's share of the group's slot
+template <int kB, int T, bool kLds, bool kNT, bool kFused, bool kPhilox>
+__global__ __launch_bounds__(kB) void k_zig_table_pass(ZigArgs a) {
+  constexpr uint32_t kWaves = kB / 64;
+  constexpr uint32_t kPerWave = zig_wave_entries(T);  // a wave's share of the group's slot
   constexpr uint32_t kRegion = kPerWave + (kFused ? 1u : 0u);  // fused: + an edge element (waves 0 and 1)
   __shared__ double2 lds_tab[kLds ? 1024 : 1];
   __shared__ uint32_t q[kWaves * kRegion];
   __shared__ uint32_t wave_n[kWaves];
-  if (kLds) {
-    for (uint32_t i = threadIdx.x; i < 1024; i += kBlock) lds_tab[i] = a.xx[i];
+  if (kLds) {  // all loads first, then all LDS writes: one L2 round trip per group
+    constexpr int kPer = 1024 / kB;
+    double2 t[kPer];
+#pragma unroll
+    for (int r = 0; r < kPer; ++r) t[r] = a.xx[threadIdx.x + r * kB];
+#pragma unroll
+    for (int r = 0; r < kPer; ++r) lds_tab[threadIdx.x + r * kB] = t[r];
     __syncthreads();
   }
   const uint32_t w = threadIdx.x >> 6;
@@ -216,8 +228,8 @@ __global__ __launch_bounds__(kBlock) void k_zig_table_pass(ZigArgs a) {
   const uint32_t share = (a.slot_cap + kWaves - 1) / kWaves;
   WaveQueue wq{q + w * kRegion, (share < kPerWave ? share : kPerWave) + (kFused ? 1u : 0u), 0u};
   const double2 *tab = kLds ? lds_tab : a.xx;
-  if (((a.start + a.head) & 1u) == 0) zig_tiles<T, true, kFused, kNT, kPhilox>(a, tab, wq);
-  else zig_tiles<T, false, kFused, kNT, kPhilox>(a, tab, wq);
+  if (((a.start + a.head) & 1u) == 0) zig_tiles<kB, T, true, kFused, kNT, kPhilox>(a, tab, wq);
+  else zig_tiles<kB, T, false, kFused, kNT, kPhilox>(a, tab, wq);
   if (blockIdx.x == 0) {  // the element before the first boundary and the one after the last vector
     const uint32_t t = threadIdx.x;
     bool edge = false;
@@ -256,15 +268,15 @@ __global__ __launch_bounds__(kBlock) void k_zig_table_pass(ZigArgs a) {
   if (kFused) {
     if (threadIdx.x == 0) a.counts[blockIdx.x] = seen;
     if (!over) {
-      for (uint32_t j = threadIdx.x; j < kept; j += kBlock) {
+      for (uint32_t j = threadIdx.x; j < kept; j += kB) {
         const uint32_t k = entry(j);
         a.out[k] = zig_slow<kPhilox>(a, k);
       }
     } else {  // a wave had more misses than its region holds: walk the group's elements again
-      const uint64_t e0 = a.head + (uint64_t)blockIdx.x * T * kBlock * 2;
-      uint64_t e1 = e0 + (uint64_t)T * kBlock * 2;
+      const uint64_t e0 = a.head + (uint64_t)blockIdx.x * T * kB * 2;
+      uint64_t e1 = e0 + (uint64_t)T * kB * 2;
       if (e1 > a.head + 2 * a.nvec) e1 = a.head + 2 * a.nvec;
-      for (uint64_t k = e0 + threadIdx.x; k < e1; k += kBlock) {
+      for (uint64_t k = e0 + threadIdx.x; k < e1; k += kB) {
         uint32_t lo, hi;
         zig_primary<kPhilox>(a, k, &lo, &hi);
         double y;
@@ -283,7 +295,7 @@ __global__ __launch_bounds__(kBlock) void k_zig_table_pass(ZigArgs a) {
     }
   } else {  // the kept entries go to the group's slot (at most kWaves * kPerWave = slot_size)
     if (threadIdx.x == 0) a.counts[blockIdx.x] = kept;
-    for (uint32_t j = threadIdx.x; j < kept; j += kBlock) a.slots[(uint64_t)blockIdx.x * a.slot_size + j] = entry(j);
+    for (uint32_t j = threadIdx.x; j < kept; j += kB) a.slots[(uint64_t)blockIdx.x * a.slot_size + j] = entry(j);
   }
 }
 
@@ -482,34 +494,57 @@ static tk_status zig_reserve(ZigDevice &d, uint64_t groups, uint64_t slot_words,
   return TK_OK;
 }
 
-template <int T, bool kLds, bool kFused, bool kPhilox>
+template <int kB, int T, bool kLds, bool kFused, bool kPhilox>
 static void launch_table_pass(const ZigArgs &a, hipStream_t stream) {
   if (config().nt_stores)
-    hipLaunchKernelGGL((k_zig_table_pass<T, kLds, true, kFused, kPhilox>), dim3(a.ngroups), dim3(kBlock), 0, stream, a);
+    hipLaunchKernelGGL((k_zig_table_pass<kB, T, kLds, true, kFused, kPhilox>), dim3(a.ngroups), dim3(kB), 0, stream, a);
   else
-    hipLaunchKernelGGL((k_zig_table_pass<T, kLds, false, kFused, kPhilox>), dim3(a.ngroups), dim3(kBlock), 0, stream,
+    hipLaunchKernelGGL((k_zig_table_pass<kB, T, kLds, false, kFused, kPhilox>), dim3(a.ngroups), dim3(kB), 0, stream,
                        a);
 }
 
+// The table-pass shapes that are built: 256-lane groups with 2 .. 16 tiles (LDS or global
+// table), or one tile gathering from the global table.  (1024-lane groups measured slower
+// at every tile count: their 16-wave slots wait for the one wave that finishes the misses.)
+struct ZigShape {
+  int block, tiles;
+  bool lds;
+};
+
+static ZigShape zig_shape() {
+  const int zt = config().zig_tiles;
+  ZigShape sh;
+  sh.block = kBlock;
+  sh.tiles = zt >= 16 ? 16 : zt >= 8 ? 8 : zt >= 4 ? 4 : zt >= 2 ? 2 : 1;
+  sh.lds = config().zig_lds && sh.tiles > 1;
+  return sh;
+}
+
 template <bool kFused, bool kPhilox>
-static void launch_table_pass(int tiles, bool lds, const ZigArgs &a, hipStream_t stream) {
-  switch (tiles) {
+static void launch_table_pass(const ZigShape &sh, const ZigArgs &a, hipStream_t stream) {
+  const bool lds = sh.lds;
+  switch (sh.tiles) {
     case 2:
-      lds ? launch_table_pass<2, true, kFused, kPhilox>(a, stream) : launch_table_pass<2, false, kFused, kPhilox>(a, stream);
+      lds ? launch_table_pass<256, 2, true, kFused, kPhilox>(a, stream)
+          : launch_table_pass<256, 2, false, kFused, kPhilox>(a, stream);
       break;
     case 4:
-      lds ? launch_table_pass<4, true, kFused, kPhilox>(a, stream) : launch_table_pass<4, false, kFused, kPhilox>(a, stream);
+      lds ? launch_table_pass<256, 4, true, kFused, kPhilox>(a, stream)
+          : launch_table_pass<256, 4, false, kFused, kPhilox>(a, stream);
       break;
     case 8:
-      lds ? launch_table_pass<8, true, kFused, kPhilox>(a, stream) : launch_table_pass<8, false, kFused, kPhilox>(a, stream);
+      lds ? launch_table_pass<256, 8, true, kFused, kPhilox>(a, stream)
+          : launch_table_pass<256, 8, false, kFused, kPhilox>(a, stream);
       break;
     case 16:
-      lds ? launch_table_pass<16, true, kFused, kPhilox>(a, stream)
-          : launch_table_pass<16, false, kFused, kPhilox>(a, stream);
+      lds ? launch_table_pass<256, 16, true, kFused, kPhilox>(a, stream)
+          : launch_table_pass<256, 16, false, kFused, kPhilox>(a, stream);
       break;
-    default: launch_table_pass<1, false, kFused, kPhilox>(a, stream); break;
+    default: launch_table_pass<256, 1, false, kFused, kPhilox>(a, stream); break;
   }
 }
+
+static uint32_t zig_slot_entries(const ZigShape &sh) { return zig_slot_entries(kBlock, sh.tiles); }
 
 // Validates and runs one f64 normal fill; the caller has set the source fields of `a`.
 // Element indices within one call are 32-bit (the miss queues hold them).
@@ -537,14 +572,12 @@ static tk_status normal_f64_fill(ZigArgs a, uint64_t start_draw, uint64_t n, uin
     std::lock_guard<std::mutex> lock(g_cap_mutex);
     if (g_debug_mode) fused = g_debug_mode == 2;
   }
-  const int zt = config().zig_tiles;
-  const int tiles = zt >= 16 ? 16 : zt >= 8 ? 8 : zt >= 4 ? 4 : zt >= 2 ? 2 : 1;
-  const bool lds = config().zig_lds && tiles > 1;
-  const uint64_t per_group = (uint64_t)kBlock * tiles;
+  const ZigShape sh = zig_shape();
+  const uint64_t per_group = (uint64_t)sh.block * sh.tiles;  // 16-byte vectors per group
   uint64_t groups = (a.nvec + per_group - 1) / per_group;
   if (groups == 0) groups = 1;
   a.ngroups = (uint32_t)groups;
-  a.slot_size = kSlotPerTile * tiles;
+  a.slot_size = zig_slot_entries(sh);
   uint64_t ovf_cap = kOvfDefault;
   {
     std::lock_guard<std::mutex> lock(g_cap_mutex);
@@ -566,14 +599,16 @@ static tk_status normal_f64_fill(ZigArgs a, uint64_t start_draw, uint64_t n, uin
   a.ctr = d.ctr;
 
   if (fused) {
-    launch_table_pass<true, kPhilox>(tiles, lds, a, stream);
+    launch_table_pass<true, kPhilox>(sh, a, stream);
     if ((st = launch_status()) != TK_OK) return st;
   } else {
     hipLaunchKernelGGL(k_zig_reset, dim3(1), dim3(64), 0, stream, d.ctr);
     if ((st = launch_status()) != TK_OK) return st;
-    launch_table_pass<false, kPhilox>(tiles, lds, a, stream);
+    launch_table_pass<false, kPhilox>(sh, a, stream);
     if ((st = launch_status()) != TK_OK) return st;
-    const uint32_t gpb = (uint32_t)(kBlock / tiles);  // table-pass groups per continuation block
+    // table-pass groups per continuation block: about 256 tiles of 256 lanes' worth
+    uint32_t gpb = (uint32_t)(kBlock * kBlock / (sh.block * sh.tiles));
+    if (gpb == 0) gpb = 1;
     const uint64_t cgrid = (groups + gpb - 1) / gpb;
     hipLaunchKernelGGL(k_zig_continue<kPhilox>, dim3((uint32_t)cgrid), dim3(kBlock), 0, stream, a, gpb);
     if ((st = launch_status()) != TK_OK) return st;
