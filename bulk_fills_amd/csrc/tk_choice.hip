@@ -158,8 +158,20 @@ __device__ __forceinline__ void choice_tiles(const ChoiceArgs &a, const uint2 *t
 template <int T, bool kLds, bool kNT, bool kPhilox>
 __global__ __launch_bounds__(kBlock) void k_choice(ChoiceArgs a) {
   extern __shared__ uint2 tab[];
-  if (kLds) {
-    for (uint32_t i = threadIdx.x; i < a.n; i += kBlock) tab[i] = a.table[i];
+  if (kLds) {  // four loads in flight per lane before the LDS writes: one L2 round trip per 4 KiB
+    for (uint32_t i0 = 0; i0 < a.n; i0 += 4 * kBlock) {
+      uint2 t[4];
+#pragma unroll
+      for (uint32_t r = 0; r < 4; ++r) {
+        const uint32_t i = i0 + r * kBlock + threadIdx.x;
+        if (i < a.n) t[r] = a.table[i];
+      }
+#pragma unroll
+      for (uint32_t r = 0; r < 4; ++r) {
+        const uint32_t i = i0 + r * kBlock + threadIdx.x;
+        if (i < a.n) tab[i] = t[r];
+      }
+    }
     __syncthreads();
   }
   if (((a.start + a.head) & 3u) == 0) choice_tiles<T, kLds, true, kNT, kPhilox>(a, tab);

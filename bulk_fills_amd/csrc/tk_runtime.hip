@@ -27,7 +27,7 @@ const Config &config() {
     c.nt_stores = st && strcmp(st, "nt") == 0;
     c.max_blocks = env_u64("TK_MAX_BLOCKS", 0x7FFFFFFFull);
     c.unroll = (int)env_u64("TK_UNROLL", 1);
-    c.choice_tiles = (int)env_u64("TK_CHOICE_TILES", 2);
+    c.choice_tiles = (int)env_u64("TK_CHOICE_TILES", 4);
     c.exp_tiles = (int)env_u64("TK_EXP_TILES", 2);
     c.zig_tiles = (int)env_u64("TK_ZIG_TILES", 4);
     const char *zt = getenv("TK_ZIG_TABLE");
