@@ -78,6 +78,7 @@ SIGNATURES = {
     "tk_debug_set_miss_capacity": [_u32, _u64],
     "tk_debug_last_miss_count": [_p],
     "tk_debug_set_normal_f64_mode": [_u32],
+    "tk_debug_set_tunable": [C.c_char_p, _i64],
 }
 for _name, _args in SIGNATURES.items():
     _fn = getattr(lib, _name)
@@ -282,6 +283,14 @@ def tk_debug_set_miss_capacity(per_group, overflow):
 
 def tk_debug_set_normal_f64_mode(mode):
     _check(lib.tk_debug_set_normal_f64_mode(mode), "tk_debug_set_normal_f64_mode")
+
+
+TUNABLES = ("store_nt", "max_blocks", "unroll", "choice_tiles", "exp_tiles", "zig_tiles", "zig_lds", "zig_fused")
+
+
+def tk_debug_set_tunable(name, value):
+    """Sets a launch tunable (see include/tk.h); a negative value restores the environment's."""
+    _check(lib.tk_debug_set_tunable(name.encode(), int(value)), "tk_debug_set_tunable")
 
 
 def tk_debug_last_miss_count():

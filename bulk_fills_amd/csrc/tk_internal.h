@@ -2,6 +2,8 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+
+#include <atomic>
 #include <stdint.h>
 
 #include <mutex>
@@ -38,17 +40,18 @@ inline uint32_t host_substream_key(uint32_t key, uint32_t purpose) {
   return host_lowbias32(host_lowbias32(host_lowbias32(key) ^ purpose));
 }
 
-// Tunables read once from the environment (benchmarks and tests only; defaults are the
-// measured best).
+// Tunables: read once from the environment (TK_*), changeable at run time through
+// tk_debug_set_tunable (benchmarks and tests only; the defaults are the measured best).
+// Host code reads them once per launch; atomics keep concurrent readers well defined.
 struct Config {
-  bool nt_stores;           // TK_STORE=nt: non-temporal 16-byte stores
-  uint64_t max_blocks;      // TK_MAX_BLOCKS: cap on the grid of the streaming fills
-  int unroll;               // TK_UNROLL: 16-byte vectors per lane per tile (1, 2 or 4)
-  int choice_tiles;         // TK_CHOICE_TILES: 4 KiB tiles per choice work-group (1, 2, 4, 8)
-  int exp_tiles;            // TK_EXP_TILES: 4 KiB tiles per exponential work-group (1, 2, 4)
-  int zig_tiles;            // TK_ZIG_TILES: tiles (one 16-byte vector per lane) per table-pass work-group
-  bool zig_fused;           // TK_ZIG_MODE=fused|split: misses finished in the table pass, or in a second kernel
-  bool zig_lds;             // TK_ZIG_TABLE=lds|global: where the table pass gathers the layers
+  std::atomic<bool> nt_stores;       // TK_STORE=nt: non-temporal 16-byte stores
+  std::atomic<uint64_t> max_blocks;  // TK_MAX_BLOCKS: cap on the grid of the streaming fills
+  std::atomic<int> unroll;           // TK_UNROLL: 16-byte vectors per lane per tile (1, 2 or 4)
+  std::atomic<int> choice_tiles;     // TK_CHOICE_TILES: 4 KiB tiles per choice work-group (1, 2, 4, 8)
+  std::atomic<int> exp_tiles;        // TK_EXP_TILES: 4 KiB tiles per exponential work-group (1, 2, 4)
+  std::atomic<int> zig_tiles;        // TK_ZIG_TILES: tiles (one 16-byte vector per lane) per table-pass work-group
+  std::atomic<bool> zig_fused;       // TK_ZIG_MODE=fused|split: misses finished in the table pass, or in a second kernel
+  std::atomic<bool> zig_lds;         // TK_ZIG_TABLE=lds|global: where the table pass gathers the layers
 };
 const Config &config();
 

@@ -2,6 +2,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <initializer_list>
 #include <mutex>
 
 #include "tk_internal.h"
@@ -20,24 +21,46 @@ static uint64_t env_u64(const char *name, uint64_t dflt) {
   return (end && *end == 0 && v > 0) ? (uint64_t)v : dflt;
 }
 
-const Config &config() {
-  static const Config cfg = [] {
-    Config c;
+// Sets one tunable from the environment (the defaults when a variable is unset).
+static bool env_tunable(Config &c, const char *name) {
+  if (!strcmp(name, "store_nt")) {
     const char *st = getenv("TK_STORE");
     c.nt_stores = st && strcmp(st, "nt") == 0;
+  } else if (!strcmp(name, "max_blocks")) {
     c.max_blocks = env_u64("TK_MAX_BLOCKS", 0x7FFFFFFFull);
+  } else if (!strcmp(name, "unroll")) {
     c.unroll = (int)env_u64("TK_UNROLL", 1);
+  } else if (!strcmp(name, "choice_tiles")) {
     c.choice_tiles = (int)env_u64("TK_CHOICE_TILES", 4);
+  } else if (!strcmp(name, "exp_tiles")) {
     c.exp_tiles = (int)env_u64("TK_EXP_TILES", 2);
+  } else if (!strcmp(name, "zig_tiles")) {
     c.zig_tiles = (int)env_u64("TK_ZIG_TILES", 4);
+  } else if (!strcmp(name, "zig_lds")) {
     const char *zt = getenv("TK_ZIG_TABLE");
     c.zig_lds = !(zt && strcmp(zt, "global") == 0);
+  } else if (!strcmp(name, "zig_fused")) {
     const char *zm = getenv("TK_ZIG_MODE");
     c.zig_fused = !(zm && strcmp(zm, "split") == 0);
-    return c;
-  }();
+  } else {
+    return false;
+  }
+  return true;
+}
+
+static const char *const kTunables[] = {"store_nt",  "max_blocks", "unroll",  "choice_tiles",
+                                        "exp_tiles", "zig_tiles",  "zig_lds", "zig_fused"};
+
+static Config &mutable_config() {
+  static Config cfg;
+  static std::once_flag once;
+  std::call_once(once, [] {
+    for (const char *name : kTunables) env_tunable(cfg, name);
+  });
   return cfg;
 }
+
+const Config &config() { return mutable_config(); }
 
 int current_device(tk_status *st) {
   int dev = -1;
@@ -82,5 +105,27 @@ const char *tk_status_string(tk_status s) {
 }
 
 int tk_last_hip_error(void) { return tk::g_last_hip_error; }
+
+tk_status tk_debug_set_tunable(const char *name, int64_t value) {
+  using namespace tk;
+  if (!name) return TK_EINVAL;
+  Config &c = mutable_config();
+  if (value < 0) return env_tunable(c, name) ? TK_OK : TK_EINVAL;  // back to the environment's value
+  const auto one_of = [value](std::initializer_list<int64_t> ok) {
+    for (int64_t v : ok)
+      if (v == value) return true;
+    return false;
+  };
+  if (!strcmp(name, "store_nt") && one_of({0, 1})) c.nt_stores = value == 1;
+  else if (!strcmp(name, "max_blocks") && value >= 1 && value <= 0x7FFFFFFF) c.max_blocks = (uint64_t)value;
+  else if (!strcmp(name, "unroll") && one_of({1, 2, 4})) c.unroll = (int)value;
+  else if (!strcmp(name, "choice_tiles") && one_of({1, 2, 4, 8})) c.choice_tiles = (int)value;
+  else if (!strcmp(name, "exp_tiles") && one_of({1, 2, 4})) c.exp_tiles = (int)value;
+  else if (!strcmp(name, "zig_tiles") && one_of({1, 2, 4, 8, 16})) c.zig_tiles = (int)value;
+  else if (!strcmp(name, "zig_lds") && one_of({0, 1})) c.zig_lds = value == 1;
+  else if (!strcmp(name, "zig_fused") && one_of({0, 1})) c.zig_fused = value == 1;
+  else return TK_EINVAL;
+  return TK_OK;
+}
 
 }  // extern "C"

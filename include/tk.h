@@ -214,6 +214,23 @@ tk_status tk_debug_set_normal_f64_mode(uint32_t mode);
 /* Test hook: waits for the current device's last tk_fill_normal_f64 and returns how many
  * of its draws missed the fast path (synchronous). */
 tk_status tk_debug_last_miss_count(uint64_t *count);
+/* Test and benchmark hook: sets a launch tunable for every later call in the process (the
+ * defaults, read from TK_* environment variables at first use, are the measured best).
+ * Results never depend on them; they choose among launch shapes that compute the same
+ * values.  `name` and the accepted values:
+ *   "store_nt" 0|1        non-temporal 16-byte stores in the streaming fills (TK_STORE=nt)
+ *   "max_blocks" 1..2^31-1  grid cap of the streaming fills, which then stride (TK_MAX_BLOCKS)
+ *   "unroll" 1|2|4        16-byte vectors per lane per tile in the streaming fills (TK_UNROLL)
+ *   "choice_tiles" 1|2|4|8  4 KiB tiles per choice work-group (TK_CHOICE_TILES)
+ *   "exp_tiles" 1|2|4     tiles per exponential work-group (TK_EXP_TILES)
+ *   "zig_tiles" 1|2|4|8|16  tiles per ziggurat table-pass work-group (TK_ZIG_TILES)
+ *   "zig_lds" 0|1         ziggurat layer gathers from an LDS copy or from L1/L2 (TK_ZIG_TABLE)
+ *   "zig_fused" 0|1       ziggurat misses finished in the table pass or a second kernel
+ *                         (TK_ZIG_MODE; tk_debug_set_normal_f64_mode overrides it)
+ * A negative value restores the environment's setting.  Unknown names or values: TK_EINVAL.
+ * Not synchronized with launches in flight on other threads beyond each value being read
+ * atomically. */
+tk_status tk_debug_set_tunable(const char *name, int64_t value);
 
 #ifdef __cplusplus
 }

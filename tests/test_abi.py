@@ -165,3 +165,29 @@ def test_binding_refuses_host_tensors_and_bad_buffers():
         tk.tk_fill_u32(1, 0, 4, torch.empty(4, dtype=torch.int32))
     with pytest.raises(ValueError, match="HIP device"):
         tk.tk_dropout_f32(1, 0, 4, 0.1, torch.empty(4), torch.empty(4))
+
+
+def test_tunable_hook_validation():
+    """tk_debug_set_tunable accepts exactly the documented names and values; a negative
+    value restores the environment's setting (no device involved)."""
+    ok = {"store_nt": (0, 1), "max_blocks": (1, 7, (1 << 31) - 1), "unroll": (1, 2, 4),
+          "choice_tiles": (1, 2, 4, 8), "exp_tiles": (1, 2, 4), "zig_tiles": (1, 2, 4, 8, 16),
+          "zig_lds": (0, 1), "zig_fused": (0, 1)}
+    bad = {"store_nt": (2,), "max_blocks": (0, 1 << 31), "unroll": (3, 8), "choice_tiles": (3, 16),
+           "exp_tiles": (8,), "zig_tiles": (3, 32), "zig_lds": (2,), "zig_fused": (7,)}
+    assert set(ok) == set(tk.TUNABLES)
+    try:
+        for name, values in ok.items():
+            for v in values:
+                assert L.tk_debug_set_tunable(name.encode(), v) == tk.TK_OK, (name, v)
+            for v in bad[name]:
+                assert L.tk_debug_set_tunable(name.encode(), v) == tk.TK_EINVAL, (name, v)
+            assert L.tk_debug_set_tunable(name.encode(), -1) == tk.TK_OK
+        assert L.tk_debug_set_tunable(b"no_such_tunable", 1) == tk.TK_EINVAL
+        assert L.tk_debug_set_tunable(b"no_such_tunable", -1) == tk.TK_EINVAL
+        assert L.tk_debug_set_tunable(None, 1) == tk.TK_EINVAL
+        with pytest.raises(tk.TkError):
+            tk.tk_debug_set_tunable("unroll", 3)
+    finally:
+        for name in tk.TUNABLES:
+            tk.tk_debug_set_tunable(name, -1)
