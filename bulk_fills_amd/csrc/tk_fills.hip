@@ -381,7 +381,7 @@ struct OpExpF64 : FillBase<uint64_t> {
 struct OpExpF32 : FillBase<uint32_t> {
   uint32_t hk;
   __device__ __forceinline__ uint32_t one(uint32_t w, const LogEntry *tab) const {
-    return __float_as_uint((float)neg_ln_unit(1.0 - (double)(w & 0xFFFFFFu) * 0x1p-24, tab));
+    return __float_as_uint(neg_ln_grid24_f32(1.0 - (double)(w & 0xFFFFFFu) * 0x1p-24, tab));
   }
   __device__ __forceinline__ uint32_t elem(uint64_t k) const { return one(word(hk, (uint32_t)(start + k)), kLogTable); }
   __device__ __forceinline__ uint4 vec(uint64_t v, const LogEntry *tab) const {
