@@ -1,29 +1,29 @@
-// tk_ziggurat.hip -- f64 normal fill: the 1024-layer ziggurat as two kernels.
+// tk_ziggurat.hip -- f64 normal fill: the 1024-layer ziggurat.
 //
 // tandem-sycl, "Design", §Normals: element i takes 64-bit draw i; about 0.43 % of draws
 // miss the fast path and continue on the per-index substream split(i) of
-// sub(key, PURPOSE_NORMAL64).  Fills of any length run two kernels:
-//   * the table pass writes every fast-path value with 16-byte stores (two elements per
-//     lane) and collects its work-group's misses through wave ballots into an LDS queue;
-//     the queue is written to the work-group's own slot of the device miss list (at most
-//     kSlot entries plus a count), so no atomic is needed.  A work-group with more misses
-//     than its slot holds (probability ~1e-10 per group) appends the rest to an
-//     overflow list with one atomic each;
-//   * the continuation pass takes the listed misses (one slot per lane) and finishes
-//     each on its substream: the wedge test against exp(-x^2/2), or the tail beyond r.
-//     If the overflow list itself overflowed it walks the whole fill instead, so the
-//     result never depends on the list sizes.
-// The fast path makes no calls, so its register footprint stays that of a streaming fill.
-// The 16 KiB layer table (pairs {X[L], X[L+1]}) lives in device memory and is read
-// through the vector caches: divergent layer reads would serialize in scalar/constant
-// memory (the page measured a drop to 27 GiB/s that way).  The table, the lists and the
-// counters are per-device state shared by all streams; fills wait on the previous
-// fill's event before touching them.
+// sub(key, PURPOSE_NORMAL64).
 //
-// The pages' design appends each group's misses with one atomic add; with the one-shot
-// grid that streams fastest on MI355X (one 4 KiB tile per group, about half a million
-// groups at 2^28 elements) that would put half a million atomics on one address, so each
-// group owns a slot instead.
+// Default (fused) path, one kernel.  Each work-group copies the 16 KiB layer table (pairs
+// {X[L] 2^-53, X[L+1]}) to LDS, writes four tiles of fast-path values with 16-byte stores
+// (two elements per lane), and queues its misses in LDS through wave ballots, one region
+// per wave, without atomics.  After a barrier it finishes its own ~9 misses (the wedge
+// test against exp(-x^2/2), or the tail beyond r) and rewrites them while their lines are
+// still in L2.  A group whose queue overflows walks its own elements again, so the result
+// never depends on the queue sizes.
+//
+// Two-kernel path (TK_ZIG_MODE=split, or tk_debug_set_normal_f64_mode(1)), the pages'
+// shape: the table pass writes each group's queue to the group's own slot of a device
+// miss list, and entries beyond the slot to an overflow list with one atomic each; the
+// continuation pass compacts the slots and finishes the misses, one per lane, and walks
+// the whole fill if the overflow list itself overflowed.  Both paths give the same values.
+//
+// The table is never read through scalar/constant memory: divergent layer reads would
+// serialize there (the page measured a drop to 27 GiB/s that way).  The table, the lists
+// and the counters are per-device state shared by all streams; fills wait on the previous
+// fill's event before touching them.  The pages append each group's misses with one
+// atomic add; at ~130 thousand groups per 2^28-element fill that would serialize on one
+// address, hence the per-group slots.
 #include <math.h>
 
 #include <mutex>
