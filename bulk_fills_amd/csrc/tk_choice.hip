@@ -98,8 +98,8 @@ __device__ __forceinline__ uint32_t choice_elem(const ChoiceArgs &a, const uint2
 
 // The eight Philox words w0 .. w0+7 of a lane whose neighbour starts at w0 + 8 (word
 // offset w0 & 3 is 0 or 2, the same for every lane).  At offset 2 the last two words are
-// the first two of the next lane's block, handed over by ds_bpermute; lane 63 computes
-// them.  Every lane of the wave must call this.
+// the first two of the next lane's block, handed over by from_next_lane (a DPP shift);
+// lane 63 computes them.  Every lane of the wave must call this.
 __device__ __forceinline__ void philox_words8(uint64_t w0, uint32_t k0, uint32_t k1, uint32_t w[8]) {
   const uint64_t b = w0 >> 2;
   const U32x4 B0 = philox4x32_10(b, k0, k1), B1 = philox4x32_10(b + 1, k0, k1);

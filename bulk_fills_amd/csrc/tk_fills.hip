@@ -1,17 +1,20 @@
-// tk_fills.hip -- streaming fill kernels: uniform, bounded, f32 normal, dropout, Philox.
+// tk_fills.hip -- streaming fill kernels: uniform, bounded, f32 normals, dropout,
+// exponentials, Philox.
 //
 // One design serves every fill here.  The output is cut into whole 16-byte vectors from
 // its first 16-byte boundary; each lane computes the draws of one vector and writes it
 // with one 16-byte store, so a wave64 store instruction covers 1 KiB of contiguous HBM.
-// A work-group handles U consecutive runs of 256 vectors (4 KiB each), one per unrolled
-// step, so U independent vectors are in flight per lane.  The few elements before the
-// first boundary and after the last whole vector are written one at a time by block 0.
+// A work-group handles U consecutive runs of 256 vectors (4 KiB each; U = 1 by default,
+// the shape that stores fastest), and the few elements before the first boundary and
+// after the last whole vector are written one at a time by block 0.
 //
 // Because every 32-bit word of the stream is its own counter, word-sized and wider draws
 // never straddle a vector.  Sub-word draws (u8, u16, f16, bool), Box-Muller pairs at odd
 // starts and Philox blocks at starts that are not a multiple of four straddle by at most
-// one word, pair or block: that piece comes from the next lane through ds_bpermute, and
-// the last lane of a wave computes it itself.  No LDS staging and no extra HBM traffic.
+// one word, pair or block: that piece comes from the next lane through a DPP row shift
+// (wave_shl:1).  The last lane of a wave computes its piece itself, except for Philox,
+// where waves store 63 vectors and lane 63 only feeds lane 62 (k_vec_fill_overlap).  No
+// LDS staging and no extra HBM traffic.
 #include "tk_device.h"
 #include "tk_internal.h"
 #include "tk_log.h"
