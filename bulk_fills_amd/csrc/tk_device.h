@@ -15,6 +15,10 @@ namespace tk {
 
 constexpr int kBlock = 256;  // work-group size: four wave64s
 
+// s_waitcnt immediate that waits for every outstanding vector memory operation of the wave
+// (gfx9 encoding: vmcnt 0, expcnt and lgkmcnt at their maxima, i.e. not waited for)
+constexpr unsigned kWaitVmcnt0 = 0x0F70u;
+
 // ---- generator and f32 uniform: the public per-element API (include/tk_device_api.h),
 // so that the fills and kernels written against that header draw the same values ------
 __device__ __forceinline__ uint32_t lowbias32(uint32_t x) { return tk_hash32(x); }

@@ -31,7 +31,7 @@ static bool env_tunable(Config &c, const char *name) {
   } else if (!strcmp(name, "unroll")) {
     c.unroll = (int)env_u64("TK_UNROLL", 1);
   } else if (!strcmp(name, "choice_tiles")) {
-    c.choice_tiles = (int)env_u64("TK_CHOICE_TILES", 4);
+    c.choice_tiles = (int)env_u64("TK_CHOICE_TILES", 2);
   } else if (!strcmp(name, "exp_tiles")) {
     c.exp_tiles = (int)env_u64("TK_EXP_TILES", 2);
   } else if (!strcmp(name, "zig_tiles")) {

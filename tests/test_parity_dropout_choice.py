@@ -61,8 +61,9 @@ def test_dropout_full_workload_sampled():
 
 
 @pytest.mark.parametrize("weights", [
-    [1.0], [2.0, 1.0], [0.0, 5.0, 0.0, 1.0], list(tk_inputs.zipf_weights()),
-    list(np.random.default_rng(9).random(5000)), list(np.random.default_rng(10).random(10000) + 0.5),
+    [1.0], [2.0, 1.0], [1.0, 2.0, 3.0], [0.0, 5.0, 0.0, 1.0], list(tk_inputs.zipf_weights()),
+    list(np.random.default_rng(9).random(5000)), list(np.random.default_rng(11).random(8191) + 0.1),
+    list(np.random.default_rng(12).random(8192) + 0.1), list(np.random.default_rng(10).random(10000) + 0.5),
 ])
 def test_choice(weights):
     table = tk.tk_alias_create(weights)

@@ -100,7 +100,7 @@ def check_all():
 CASES = [
     ("unroll", 2, check_streaming), ("unroll", 4, check_streaming),
     ("max_blocks", 7, check_streaming), ("store_nt", 1, check_all),
-    ("choice_tiles", 1, check_choice), ("choice_tiles", 2, check_choice), ("choice_tiles", 8, check_choice),
+    ("choice_tiles", 1, check_choice), ("choice_tiles", 4, check_choice), ("choice_tiles", 8, check_choice),
     ("exp_tiles", 1, check_exponential), ("exp_tiles", 4, check_exponential),
     ("zig_tiles", 1, check_normal_f64), ("zig_tiles", 2, check_normal_f64), ("zig_tiles", 8, check_normal_f64),
     ("zig_tiles", 16, check_normal_f64), ("zig_lds", 0, check_normal_f64), ("zig_fused", 0, check_normal_f64),
