@@ -19,9 +19,11 @@
 // the whole fill if the overflow list itself overflowed.  Both paths give the same values.
 //
 // The table is never read through scalar/constant memory: divergent layer reads would
-// serialize there (the page measured a drop to 27 GiB/s that way).  The table, the lists
-// and the counters are per-device state shared by all streams; fills wait on the previous
-// fill's event before touching them.  The pages append each group's misses with one
+// serialize there (the page measured a drop to 27 GiB/s that way).  The table is constant
+// per-device state.  The lists and the counters are per-device state shared by all
+// streams: fills that use them (the two-kernel path, and fills counted for the miss-count
+// test hook) wait on the previous such fill's event.  The default fused fill uses none of
+// them and needs no event.  The pages append each group's misses with one
 // atomic add; at ~130 thousand groups per 2^28-element fill that would serialize on one
 // address, hence the per-group slots.
 #include <math.h>
@@ -60,7 +62,7 @@ struct ZigArgs {
   uint32_t ngroups;    // table-pass work-groups = slots
   uint32_t slot_size;  // entries reserved per slot
   uint32_t slot_cap;   // entries used per slot (<= slot_size)
-  uint32_t *counts;    // [ngroups] misses kept in each slot
+  uint32_t *counts;    // [ngroups] misses kept in each slot (fused: seen; null when not counted)
   uint32_t *slots;     // [ngroups * slot_size]
   uint32_t *ovf;       // overflow list
   uint32_t ovf_cap;
@@ -266,7 +268,7 @@ __global__ __launch_bounds__(kB) void k_zig_table_pass(ZigArgs a) {
     return q[i * kRegion + (j - off[i])];
   };
   if (kFused) {
-    if (threadIdx.x == 0) a.counts[blockIdx.x] = seen;
+    if (threadIdx.x == 0 && a.counts) a.counts[blockIdx.x] = seen;
     if (!over) {
       for (uint32_t j = threadIdx.x; j < kept; j += kB) {
         const uint32_t k = entry(j);
@@ -435,8 +437,9 @@ struct ZigDevice {
   uint64_t slot_words = 0;    // slot entries allocated
   uint32_t *ovf = nullptr;
   uint64_t ovf_alloc = 0;
-  uint64_t last_groups = 0;   // table-pass groups of the last fill
+  uint64_t last_groups = 0;   // table-pass groups of the last counted fill
   bool last_fused = false;
+  bool last_counted = false;  // the last fill on this device kept its miss counts
   hipEvent_t last = nullptr;
   bool recorded = false;
 };
@@ -568,10 +571,21 @@ static tk_status normal_f64_fill(ZigArgs a, uint64_t start_draw, uint64_t n, uin
   a.tail = (uint32_t)(n - a.head - 2 * a.nvec);
   a.r = TK_ZIG_R;
   bool fused = config().zig_fused;
+  bool counted = false;  // per-group miss counts kept for tk_debug_last_miss_count
   {
     std::lock_guard<std::mutex> lock(g_cap_mutex);
-    if (g_debug_mode) fused = g_debug_mode == 2;
+    if (g_debug_mode) {
+      fused = g_debug_mode == 2;
+      counted = true;
+    }
   }
+  // The two-kernel path shares the per-device lists and counters between fills (its
+  // per-group counts are always kept), and a counted fused fill the count array: such
+  // fills are ordered by the device's event.  The default fused fill reads only the
+  // constant layer tables, so it shares nothing mutable and enqueues its kernel alone (an
+  // event record per fill left ~6 us idle after each 2^28-element fill on MI355X).
+  if (!fused) counted = true;
+  const bool shared = counted;
   const ZigShape sh = zig_shape();
   const uint64_t per_group = (uint64_t)sh.block * sh.tiles;  // 16-byte vectors per group
   uint64_t groups = (a.nvec + per_group - 1) / per_group;
@@ -589,11 +603,13 @@ static tk_status normal_f64_fill(ZigArgs a, uint64_t start_draw, uint64_t n, uin
   ZigDevice &d = g_zig[dev];
   std::lock_guard<std::mutex> lock(d.m);
   if ((st = zig_init(d)) != TK_OK) return st;
-  if ((st = zig_reserve(d, groups, fused ? 0 : groups * a.slot_size, fused ? 0 : ovf_cap)) != TK_OK) return st;
-  if (d.recorded && (st = hip_status(hipStreamWaitEvent(stream, d.last, 0))) != TK_OK) return st;
+  if (shared) {
+    if ((st = zig_reserve(d, groups, fused ? 0 : groups * a.slot_size, fused ? 0 : ovf_cap)) != TK_OK) return st;
+    if (d.recorded && (st = hip_status(hipStreamWaitEvent(stream, d.last, 0))) != TK_OK) return st;
+  }
   a.xx = d.xx;
   a.f = d.f;
-  a.counts = d.counts;
+  a.counts = shared ? d.counts : nullptr;
   a.slots = d.slots;
   a.ovf = d.ovf;
   a.ctr = d.ctr;
@@ -613,6 +629,8 @@ static tk_status normal_f64_fill(ZigArgs a, uint64_t start_draw, uint64_t n, uin
     hipLaunchKernelGGL(k_zig_continue<kPhilox>, dim3((uint32_t)cgrid), dim3(kBlock), 0, stream, a, gpb);
     if ((st = launch_status()) != TK_OK) return st;
   }
+  d.last_counted = counted;
+  if (!shared) return TK_OK;
   if ((st = hip_status(hipEventRecord(d.last, stream))) != TK_OK) return st;
   d.recorded = true;
   d.last_groups = groups;
@@ -675,6 +693,7 @@ tk_status tk_debug_last_miss_count(uint64_t *count) {
     *count = 0;
     return TK_OK;
   }
+  if (!d.last_counted) return TK_EINVAL;  // the last fill kept no counts
   if ((st = hip_status(hipEventSynchronize(d.last))) != TK_OK) return st;
   // every miss sits in a group's count or, in the two-kernel mode, in the overflow count
   std::vector<uint32_t> v(d.last_groups);

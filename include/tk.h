@@ -95,8 +95,11 @@ tk_status tk_fill_i64_below(uint32_t key, uint64_t start_draw, uint64_t n, int64
  * per-index substream split(i) of sub(key, "NORM") (wedge test against exp(-x^2/2), or
  * the tail beyond r).  A table pass writes the fast-path values; the misses are finished
  * either by the same work-group after its stores or by a continuation pass over a miss
- * list (tk_debug_set_normal_f64_mode); the lists and the 16 KiB layer table are
- * per-device library state, ordered across streams by an event.  i < 2^31.
+ * list (tk_debug_set_normal_f64_mode).  The 16 KiB layer table is constant per-device
+ * library state; the miss lists and counts of the two-kernel path (and of counted test
+ * fills) are per-device state ordered across streams by an event, while the default fused
+ * fill keeps no mutable state and runs concurrently with fills on other streams.
+ * i < 2^31.
  * f32 (tandem-sycl, "Design", §Normals; Phobos, §randn): Box-Muller pairs; draw i
  * belongs to pair c = i >> 1 built from the f32 uniforms at words 2c and 2c+1:
  * r = sqrt(-2 ln(1 - u1)), angle 2 pi t with t = u2 wrapped into [-1/2, 1/2); even i
@@ -212,7 +215,10 @@ tk_status tk_debug_set_miss_capacity(uint32_t per_group, uint64_t overflow);
  * stores), 0 = the library default.  Both give identical results. */
 tk_status tk_debug_set_normal_f64_mode(uint32_t mode);
 /* Test hook: waits for the current device's last tk_fill_normal_f64 and returns how many
- * of its draws missed the fast path (synchronous). */
+ * of its draws missed the fast path (synchronous).  The counts are kept only while a mode
+ * is chosen with tk_debug_set_normal_f64_mode (1 or 2), or when the library default is
+ * the two-kernel path; after a fill in the default fused mode, which keeps no per-device
+ * state and is not ordered against fills on other streams, it returns TK_EINVAL. */
 tk_status tk_debug_last_miss_count(uint64_t *count);
 /* Test and benchmark hook: sets a launch tunable for every later call in the process (the
  * defaults, read from TK_* environment variables at first use, are the measured best).
