@@ -102,6 +102,47 @@ def build_step(tk, torch, n):
     return fills, next_rows, calib, (out, x, table)
 
 
+class FenceFreeEvent:
+    """A HIP timing event created with hipEventDisableSystemFence and recorded on torch's
+    current stream (the stream the fills are launched on).  torch's own events perform a
+    system-scope fence when they are recorded, a cache writeback and invalidation between
+    two kernels; these mark the same point in the stream without it, so the time between a
+    pair is the launch's own.  The HIP runtime is the one libtk.so is linked against, the
+    runtime torch loaded, reached through the library's handle."""
+    FLAG = 0x20000000  # hipEventDisableSystemFence (hip_runtime_api.h)
+
+    def __init__(self, hip):
+        import ctypes as C
+        self.C, self.hip = C, hip
+        hip.hipEventCreateWithFlags.argtypes = [C.POINTER(C.c_void_p), C.c_uint]
+        hip.hipEventRecord.argtypes = [C.c_void_p, C.c_void_p]
+        hip.hipEventSynchronize.argtypes = [C.c_void_p]
+        hip.hipEventElapsedTime.argtypes = [C.POINTER(C.c_float), C.c_void_p, C.c_void_p]
+        hip.hipEventDestroy.argtypes = [C.c_void_p]
+        self.e = C.c_void_p()
+        self._check(hip.hipEventCreateWithFlags(C.byref(self.e), self.FLAG), "hipEventCreateWithFlags")
+
+    @staticmethod
+    def _check(code, what):
+        if code != 0:
+            raise RuntimeError(f"{what} failed: hipError {code}")
+
+    def record(self):
+        import torch
+        self._check(self.hip.hipEventRecord(self.e, self.C.c_void_p(torch.cuda.current_stream().cuda_stream)),
+                    "hipEventRecord")
+
+    def elapsed_time(self, end):
+        self._check(self.hip.hipEventSynchronize(end.e), "hipEventSynchronize")
+        ms = self.C.c_float()
+        self._check(self.hip.hipEventElapsedTime(self.C.byref(ms), self.e, end.e), "hipEventElapsedTime")
+        return ms.value
+
+    def __del__(self):
+        if self.e:
+            self.hip.hipEventDestroy(self.e)
+
+
 def measured_traffic(fill):
     """HBM bytes per launch of `fill`'s kernel from the committed rocprofv3 counter record
     (FETCH_SIZE and WRITE_SIZE scaled by a copy-kernel calibration), or None when there is
@@ -228,8 +269,9 @@ def main():
     dj = [f[0] for f in fills].index(dom)
 
     # timed region: K steps; the only instrumentation is an event pair around the dominant
-    # fill's launch, on the stream it is launched on (torch's current stream)
-    dev = [{dj: pairs()} for _ in range(K)]
+    # fill's launch, on the stream it is launched on (torch's current stream), without the
+    # system-scope fence torch's events would add
+    dev = [{dj: (FenceFreeEvent(tk.lib), FenceFreeEvent(tk.lib))} for _ in range(K)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(K):
