@@ -689,11 +689,11 @@ tk_status tk_debug_last_miss_count(uint64_t *count) {
   if (dev < 0) return st;
   ZigDevice &d = g_zig[dev];
   std::lock_guard<std::mutex> lock(d.m);
-  if (!d.ready || !d.recorded) {
+  if (!d.ready) {  // no fill on this device yet
     *count = 0;
     return TK_OK;
   }
-  if (!d.last_counted) return TK_EINVAL;  // the last fill kept no counts
+  if (!d.last_counted || !d.recorded) return TK_EINVAL;  // the last fill kept no counts
   if ((st = hip_status(hipEventSynchronize(d.last))) != TK_OK) return st;
   // every miss sits in a group's count or, in the two-kernel mode, in the overflow count
   std::vector<uint32_t> v(d.last_groups);
