@@ -25,9 +25,9 @@
  * Tsang (2000) for the ziggurat construction, Lemire (2019) for the exact rejection
  * threshold, Vose (1991) for the alias table, Salmon et al. (SC'11) for Philox4x32-10.
  *
- * Parity unpinned: orc_philox_* (no known-answer vectors are available to check the
- * Philox word source against; only the shared definition and statistics tie it down,
- * and the Philox bounded, choice and normal variants reduce to pinned maps over it).
+ * orc_philox_*: the Philox4x32-10 word source is pinned against rocRAND's implementation
+ * (seeds, offsets past 2^34 words, every output ordering); the Philox bounded, choice and
+ * normal variants reduce to pinned maps over it.
  */
 #ifndef BULK_FILLS_ORACLE_H
 #define BULK_FILLS_ORACLE_H

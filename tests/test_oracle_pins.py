@@ -601,8 +601,8 @@ def test_choice_matches_exact_probabilities():
 
 
 # ---------------------------------------------------------------------------------------
-# Philox4x32-10: parity unpinned (no known-answer vectors here); layout, statistics and
-# inversion of the rounds only
+# Philox4x32-10: layout, statistics and inversion of the rounds here; its words equal
+# rocRAND's (tests/test_oracle_philox_rocrand.py, which needs a HIP device)
 # ---------------------------------------------------------------------------------------
 
 def test_philox_layout_and_statistics():
@@ -644,8 +644,8 @@ def test_philox_blocks_invert_to_their_counters():
     """Structure pin: running ten inverse rounds (each undone from the round's definition,
     not by re-running it) over the oracle's block must give back the counter it was asked
     for, for counters in all four lanes.  A slip in the lane order, the hi/lo halves, the
-    key words or the key schedule would not invert.  The constants themselves and the
-    output order stay unpinned against a third party."""
+    key words or the key schedule would not invert.  The constants and the output order are
+    pinned by the comparison with rocRAND."""
     rng = np.random.default_rng(7)
     for key in (0, 1, 0xFFFFFFFFFFFFFFFF, 0x0123456789ABCDEF, int(rng.integers(0, 1 << 63))):
         for b in (0, 1, (1 << 32) + 5, (1 << 62) - 1):  # primary blocks: counter (lo32 b, hi32 b, 0, 0)
@@ -724,7 +724,7 @@ def test_exponential_f64_accuracy_and_law():
 # ---------------------------------------------------------------------------------------
 # Generator and normal variants: Philox sources for the bounded, choice and normal fills;
 # the pages' half-turn Box-Muller (tandem-sycl "Design" §Normals); Phobos's one normal per
-# counter (§randn).  The Philox word source stays parity unpinned; these pins tie each
+# counter (§randn).  The Philox word source is pinned against rocRAND; these pins tie each
 # variant to the maps and laws pinned above.
 # ---------------------------------------------------------------------------------------
 PK = 0x0123456789ABCDEF
