@@ -663,7 +663,8 @@ int orc_fill_choice_u32(uint32_t key, uint64_t start, uint64_t n, const uint64_t
  * (hi(lane2 product) ^ lane1 ^ k0, lo(lane2 product), hi(lane0 product) ^ lane3 ^ k1,
  * lo(lane0 product)); the key is bumped by 0x9E3779B9 and 0xBB67AE85 between rounds.
  * Pinned against rocRAND's Philox4x32-10 (an independent implementation): its words for
- * seed s from offset o equal these for key s from word o (tests/test_oracle_philox_rocrand.py).
+ * seed s, subsequence q and offset o equal these for key s and counter words 2-3 = q, from
+ * word o (tests/test_oracle_philox_rocrand.py).
  * ------------------------------------------------------------------------------- */
 static void philox_block(uint64_t key, const uint32_t ctr[4], uint32_t out[4])
 {
@@ -732,9 +733,8 @@ int orc_philox_fill_f64(uint64_t key, uint64_t start, uint64_t n, const uint64_t
 /* ---------------------------------------------------------------------------------
  * Philox variants of the bounded, choice and normal fills: the same definitions as the
  * lowbias32 fills above over the Philox source (src_t): word i, 64-bit draw i, and the
- * per-draw substreams with counter (lo32 i, hi32 i, P, j >> 2).  The word source is pinned
- * against rocRAND at counters whose words 2 and 3 are zero; at the substreams' counters
- * only by the inversion of its rounds.
+ * per-draw substreams with counter (lo32 i, hi32 i, P, j >> 2).  The word source, primary
+ * and substream counters alike, is pinned against rocRAND's engine.
  * ------------------------------------------------------------------------------- */
 /* Substream word j of draw i for purpose P (exposed for the tests). */
 uint32_t orc_philox_sub_word(uint64_t key, uint64_t i, uint32_t purpose, uint32_t j)

@@ -26,8 +26,8 @@
  * threshold, Vose (1991) for the alias table, Salmon et al. (SC'11) for Philox4x32-10.
  *
  * orc_philox_*: the Philox4x32-10 word source is pinned against rocRAND's implementation
- * (seeds, offsets past 2^34 words, every output ordering); the Philox bounded, choice and
- * normal variants reduce to pinned maps over it.
+ * (primary and substream counters, offsets past 2^34 words); the Philox bounded, choice
+ * and normal variants reduce to pinned maps over it.
  */
 #ifndef BULK_FILLS_ORACLE_H
 #define BULK_FILLS_ORACLE_H
