@@ -25,6 +25,12 @@
  *     enqueued.  n == 0 is TK_OK and enqueues nothing.  There is no CPU fallback.
  *   - TK_EHIP reports a HIP runtime failure; tk_last_hip_error() gives its code for the
  *     calling thread.
+ *   - HIP graphs: a fill enqueues only kernel launches on `stream`, so it can be captured
+ *     into a graph and replayed.  The first f64 normal fill on a device creates the
+ *     library's per-device tables (an allocation and a copy), so run it once before
+ *     capturing; alias tables are built and uploaded by tk_alias_create, outside any
+ *     capture.  The test-hook modes of tk_debug_set_normal_f64_mode and the two-kernel
+ *     path order fills by an event and are not meant for capture.
  */
 #ifndef TK_H
 #define TK_H
