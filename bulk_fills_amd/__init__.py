@@ -79,6 +79,8 @@ SIGNATURES = {
     "tk_debug_last_miss_count": [_p],
     "tk_debug_set_normal_f64_mode": [_u32],
     "tk_debug_set_tunable": [C.c_char_p, _i64],
+    "tk_debug_fail_allocations": [_u32, _u32],
+    "tk_debug_device_bytes": [_p],
 }
 for _name, _args in SIGNATURES.items():
     _fn = getattr(lib, _name)
@@ -291,6 +293,16 @@ TUNABLES = ("store_nt", "max_blocks", "unroll", "choice_tiles", "exp_tiles", "zi
 def tk_debug_set_tunable(name, value):
     """Sets a launch tunable (see include/tk.h); a negative value restores the environment's."""
     _check(lib.tk_debug_set_tunable(name.encode(), int(value)), "tk_debug_set_tunable")
+
+
+def tk_debug_fail_allocations(skip, count):
+    _check(lib.tk_debug_fail_allocations(skip, count), "tk_debug_fail_allocations")
+
+
+def tk_debug_device_bytes():
+    v = C.c_uint64()
+    _check(lib.tk_debug_device_bytes(C.byref(v)), "tk_debug_device_bytes")
+    return v.value
 
 
 def tk_debug_last_miss_count():

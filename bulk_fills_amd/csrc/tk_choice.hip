@@ -264,12 +264,12 @@ tk_status tk_alias_create(const double *weights, uint32_t n, tk_alias **table) {
   const uint32_t padded = (n + 1) & ~1u;
   std::vector<uint2> packed(padded, make_uint2(0u, 0u));
   for (uint32_t j = 0; j < n; ++j) packed[j] = make_uint2(t->q[j], t->alias[j]);
-  if (hipMalloc(&t->table, padded * sizeof(uint2)) != hipSuccess) {
+  if (device_alloc((void **)&t->table, padded * sizeof(uint2)) != hipSuccess) {
     delete t;
     return TK_ENOMEM;
   }
   if ((st = hip_status(hipMemcpy(t->table, packed.data(), padded * sizeof(uint2), hipMemcpyHostToDevice))) != TK_OK) {
-    (void)hipFree(t->table);
+    (void)device_free(t->table, padded * sizeof(uint2));
     delete t;
     return st;
   }
@@ -280,7 +280,7 @@ tk_status tk_alias_create(const double *weights, uint32_t n, tk_alias **table) {
 tk_status tk_alias_destroy(tk_alias *t) {
   if (!t) return TK_EINVAL;
   tk_status st = TK_OK;
-  if (t->table) st = hip_status(hipFree(t->table));
+  if (t->table) st = hip_status(device_free(t->table, ((t->n + 1) & ~1u) * sizeof(uint2)));
   delete t;
   return st;
 }

@@ -63,4 +63,11 @@ int current_device(tk_status *st);
 
 constexpr int kMaxDevices = 64;
 
+// Every device allocation of the library goes through these two: they keep the count of
+// bytes the library holds (tk_debug_device_bytes) and fail the allocations a test asks to
+// fail (tk_debug_fail_allocations) without calling HIP.  device_free(nullptr, ..) does
+// nothing; `bytes` is the size the allocation was made with.
+hipError_t device_alloc(void **p, size_t bytes);
+hipError_t device_free(void *p, size_t bytes);
+
 }  // namespace tk

@@ -77,6 +77,40 @@ int current_device(tk_status *st) {
   return dev;
 }
 
+static std::mutex g_alloc_mutex;
+static uint32_t g_alloc_skip = 0;  // allocations still to succeed before the forced failures
+static uint32_t g_alloc_fail = 0;  // forced failures still to come
+static std::atomic<uint64_t> g_device_bytes{0};
+
+hipError_t device_alloc(void **p, size_t bytes) {
+  *p = nullptr;
+  {
+    std::lock_guard<std::mutex> lock(g_alloc_mutex);
+    if (g_alloc_skip > 0) {
+      --g_alloc_skip;
+    } else if (g_alloc_fail > 0) {
+      --g_alloc_fail;
+      return hipErrorOutOfMemory;
+    }
+  }
+  const hipError_t e = hipMalloc(p, bytes);
+  if (e != hipSuccess) {
+    *p = nullptr;
+    // HIP keeps a failed call's error for hipGetLastError; clear it so that the next
+    // launch's status check does not report this allocation as a launch failure
+    (void)hipGetLastError();
+    return e;
+  }
+  g_device_bytes += bytes;
+  return hipSuccess;
+}
+
+hipError_t device_free(void *p, size_t bytes) {
+  if (!p) return hipSuccess;
+  g_device_bytes -= bytes;
+  return hipFree(p);
+}
+
 int device_cus(int device) {
   static int cus[kMaxDevices];
   static std::mutex m;
@@ -105,6 +139,19 @@ const char *tk_status_string(tk_status s) {
 }
 
 int tk_last_hip_error(void) { return tk::g_last_hip_error; }
+
+tk_status tk_debug_fail_allocations(uint32_t skip, uint32_t count) {
+  std::lock_guard<std::mutex> lock(tk::g_alloc_mutex);
+  tk::g_alloc_skip = count ? skip : 0;
+  tk::g_alloc_fail = count;
+  return TK_OK;
+}
+
+tk_status tk_debug_device_bytes(uint64_t *bytes) {
+  if (!bytes) return TK_EINVAL;
+  *bytes = tk::g_device_bytes.load();
+  return TK_OK;
+}
 
 tk_status tk_debug_set_tunable(const char *name, int64_t value) {
   using namespace tk;

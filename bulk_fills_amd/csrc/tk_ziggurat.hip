@@ -451,50 +451,91 @@ static int g_debug_mode = 0;  // 0: configured default, 1: two kernels, 2: fused
 static uint64_t g_debug_ovf_cap = 0;
 constexpr uint64_t kOvfDefault = 65536;
 
-static tk_status zig_init(ZigDevice &d) {
-  if (d.ready) return TK_OK;
+// Releases the constant tables, the counter and the event (a failed first fill).
+static void zig_release(ZigDevice &d) {
+  (void)device_free(d.xx, TK_ZIG_LAYERS * sizeof(double2));
+  (void)device_free(d.f, sizeof(tk_zig_f));
+  (void)device_free(d.ctr, 4 * sizeof(uint32_t));
+  d.xx = nullptr;
+  d.f = nullptr;
+  d.ctr = nullptr;
+  if (d.last) (void)hipEventDestroy(d.last);
+  d.last = nullptr;
+}
+
+static tk_status zig_create(ZigDevice &d) {
   double2 pairs[TK_ZIG_LAYERS];
   for (int L = 0; L < TK_ZIG_LAYERS; ++L) pairs[L] = make_double2(tk_zig_x[L] * 0x1p-53, tk_zig_x[L + 1]);
-  if (hipMalloc(&d.xx, sizeof(pairs)) != hipSuccess) return TK_ENOMEM;
-  if (hipMalloc(&d.f, sizeof(tk_zig_f)) != hipSuccess) return TK_ENOMEM;
-  if (hipMalloc(&d.ctr, 4 * sizeof(uint32_t)) != hipSuccess) return TK_ENOMEM;
+  if (device_alloc((void **)&d.xx, sizeof(pairs)) != hipSuccess) return TK_ENOMEM;
+  if (device_alloc((void **)&d.f, sizeof(tk_zig_f)) != hipSuccess) return TK_ENOMEM;
+  if (device_alloc((void **)&d.ctr, 4 * sizeof(uint32_t)) != hipSuccess) return TK_ENOMEM;
   tk_status st;
   if ((st = hip_status(hipMemcpy(d.xx, pairs, sizeof(pairs), hipMemcpyHostToDevice))) != TK_OK) return st;
   if ((st = hip_status(hipMemcpy(d.f, tk_zig_f, sizeof(tk_zig_f), hipMemcpyHostToDevice))) != TK_OK) return st;
   if ((st = hip_status(hipMemset(d.ctr, 0, 4 * sizeof(uint32_t)))) != TK_OK) return st;
-  if ((st = hip_status(hipEventCreateWithFlags(&d.last, hipEventDisableTiming))) != TK_OK) return st;
-  d.ready = true;
-  return TK_OK;
+  return hip_status(hipEventCreateWithFlags(&d.last, hipEventDisableTiming));
 }
 
-// Grows the slot arrays and the overflow list; the previous fill may still read them, so
-// it is waited for first.
+// The device's state on its first fill; a failure releases whatever was created, so the
+// next fill starts again from nothing.
+static tk_status zig_init(ZigDevice &d) {
+  if (d.ready) return TK_OK;
+  const tk_status st = zig_create(d);
+  if (st != TK_OK)
+    zig_release(d);
+  else
+    d.ready = true;
+  return st;
+}
+
+// Releases the miss counts, the slot arrays and the overflow list; the last fill's miss
+// count goes with them.
+static void zig_release_lists(ZigDevice &d) {
+  (void)device_free(d.counts, d.groups_cap * sizeof(uint32_t));
+  (void)device_free(d.slots, d.slot_words * sizeof(uint32_t));
+  (void)device_free(d.ovf, d.ovf_alloc * sizeof(uint32_t));
+  d.counts = d.slots = d.ovf = nullptr;
+  d.groups_cap = d.slot_words = d.ovf_alloc = 0;
+  d.last_counted = false;
+}
+
+// Grows the miss counts, the slot arrays and the overflow list; the previous fill may
+// still read them, so it is waited for first.  If an allocation fails, all three are
+// released (the next fill allocates them again).
 static tk_status zig_reserve(ZigDevice &d, uint64_t groups, uint64_t slot_words, uint64_t ovf_cap) {
   if (groups <= d.groups_cap && slot_words <= d.slot_words && ovf_cap <= d.ovf_alloc) return TK_OK;
   tk_status st;
   if (d.recorded && (st = hip_status(hipEventSynchronize(d.last))) != TK_OK) return st;
+  st = TK_OK;
   if (groups > d.groups_cap) {
-    if (d.counts) (void)hipFree(d.counts);
+    (void)device_free(d.counts, d.groups_cap * sizeof(uint32_t));
     d.counts = nullptr;
     d.groups_cap = 0;
-    if (hipMalloc(&d.counts, groups * sizeof(uint32_t)) != hipSuccess) return TK_ENOMEM;
-    d.groups_cap = groups;
+    if (device_alloc((void **)&d.counts, groups * sizeof(uint32_t)) == hipSuccess)
+      d.groups_cap = groups;
+    else
+      st = TK_ENOMEM;
   }
-  if (slot_words > d.slot_words) {
-    if (d.slots) (void)hipFree(d.slots);
+  if (st == TK_OK && slot_words > d.slot_words) {
+    (void)device_free(d.slots, d.slot_words * sizeof(uint32_t));
     d.slots = nullptr;
     d.slot_words = 0;
-    if (hipMalloc(&d.slots, slot_words * sizeof(uint32_t)) != hipSuccess) return TK_ENOMEM;
-    d.slot_words = slot_words;
+    if (device_alloc((void **)&d.slots, slot_words * sizeof(uint32_t)) == hipSuccess)
+      d.slot_words = slot_words;
+    else
+      st = TK_ENOMEM;
   }
-  if (ovf_cap > d.ovf_alloc) {
-    if (d.ovf) (void)hipFree(d.ovf);
+  if (st == TK_OK && ovf_cap > d.ovf_alloc) {
+    (void)device_free(d.ovf, d.ovf_alloc * sizeof(uint32_t));
     d.ovf = nullptr;
     d.ovf_alloc = 0;
-    if (hipMalloc(&d.ovf, ovf_cap * sizeof(uint32_t)) != hipSuccess) return TK_ENOMEM;
-    d.ovf_alloc = ovf_cap;
+    if (device_alloc((void **)&d.ovf, ovf_cap * sizeof(uint32_t)) == hipSuccess)
+      d.ovf_alloc = ovf_cap;
+    else
+      st = TK_ENOMEM;
   }
-  return TK_OK;
+  if (st != TK_OK) zig_release_lists(d);
+  return st;
 }
 
 template <int kB, int T, bool kLds, bool kFused, bool kPhilox>

@@ -226,6 +226,18 @@ tk_status tk_debug_set_normal_f64_mode(uint32_t mode);
  * the two-kernel path; after a fill in the default fused mode, which keeps no per-device
  * state and is not ordered against fills on other streams, it returns TK_EINVAL. */
 tk_status tk_debug_last_miss_count(uint64_t *count);
+/* Test hook: of the library's next device allocations (a device's ziggurat tables on its
+ * first f64 normal fill, the two-kernel path's miss lists as they grow, alias tables), the
+ * first `skip` proceed and the `count` after them fail as if device memory were exhausted,
+ * without calling HIP.  The call that needed the memory returns TK_ENOMEM, enqueues
+ * nothing and holds no more device memory than before it (a first fill releases the
+ * tables it created; a failed growth releases all the miss lists); a later call allocates
+ * again.  count = 0 cancels.  Process-wide, for every device and thread.  A real
+ * allocation failure takes the same path. */
+tk_status tk_debug_fail_allocations(uint32_t skip, uint32_t count);
+/* Test hook: the device memory the library holds now, in bytes, over all devices: the
+ * per-device ziggurat state (held until the process ends) and the live alias tables. */
+tk_status tk_debug_device_bytes(uint64_t *bytes);
 /* Test and benchmark hook: sets a launch tunable for every later call in the process (the
  * defaults, read from TK_* environment variables at first use, are the measured best).
  * Results never depend on them; they choose among launch shapes that compute the same

@@ -1,0 +1,36 @@
+"""Device allocation failure, forced through tk_debug_fail_allocations.
+
+The library allocates device memory in three places: a device's ziggurat tables on its
+first f64 normal fill, the two-kernel path's miss lists as they grow, and alias tables.
+A failure there must return TK_ENOMEM, enqueue nothing, keep no memory the call had taken,
+and let a later call allocate again.  The GPU case runs tests/alloc_failure_child.py in a
+process of its own, since the per-device tables of this process may already exist."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+import bulk_fills_amd as tk
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+
+
+def test_hooks_without_a_device():
+    assert tk.lib.tk_debug_device_bytes(None) == tk.TK_EINVAL
+    assert tk.tk_debug_device_bytes() == 0  # nothing allocated without a fill
+    tk.tk_debug_fail_allocations(2, 3)
+    tk.tk_debug_fail_allocations(0, 0)
+
+
+@pytest.mark.gpu
+def test_forced_failures_in_a_fresh_process():
+    env = dict(os.environ)
+    env["PYTHONPATH"] = os.pathsep.join([ROOT, HERE] + [p for p in [env.get("PYTHONPATH")] if p])
+    print("alloc_failure_child.py", flush=True)
+    r = subprocess.run([sys.executable, "-u", os.path.join(HERE, "alloc_failure_child.py")], cwd=ROOT, env=env,
+                       capture_output=True, text=True, timeout=110)
+    print(r.stdout[-4000:], r.stderr[-4000:], flush=True)
+    assert r.returncode == 0, f"exit status {r.returncode}"
+    assert "alloc_failure_child: ok" in r.stdout
