@@ -197,6 +197,20 @@ def cpu_baseline(n_sample):
                       f"(single-threaded C oracle, {total_s:.1f} s)"}
 
 
+def device_info():
+    """What the numbers were measured on: device, architecture, compute units, HBM, HIP runtime."""
+    import ctypes as C
+    import torch
+    import bulk_fills_amd as tk
+    props = torch.cuda.get_device_properties(0)
+    ver = C.c_int(0)
+    tk.lib.hipRuntimeGetVersion.argtypes = [C.POINTER(C.c_int)]
+    hip_rt = ver.value if tk.lib.hipRuntimeGetVersion(C.byref(ver)) == 0 else None
+    return {"name": props.name, "gfx_arch": getattr(props, "gcnArchName", None),
+            "compute_units": props.multi_processor_count, "hbm_gib": round(props.total_memory / GIB, 1),
+            "hip_runtime_version": hip_rt, "torch": torch.__version__, "torch_hip": torch.version.hip}
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -323,7 +337,7 @@ def main():
         "fills": {k: {"GiB_per_s": round(v["GiB_per_s"], 1), "batched_ms": round(v["batched_ms"], 4),
                       "event_pair_median_ms": round(v["median_ms"], 4)} for k, v in per_fill.items()},
         "next_rows": nxt,
-        "device": torch.cuda.get_device_name(0),
+        "device": device_info(),
     }
     print(json.dumps(rec), flush=True)
     del keep
