@@ -177,11 +177,10 @@ __global__ __launch_bounds__(kBlock) void k_choice(ChoiceArgs a) {
   }
   if (((a.start + a.head) & 3u) == 0) choice_tiles<T, kLds, true, kNT, kPhilox>(a, tab);
   else choice_tiles<T, kLds, false, kNT, kPhilox>(a, tab);
-  if (blockIdx.x == 0) {
-    const uint32_t t = threadIdx.x;
-    if (t < a.head) a.out[t] = choice_elem<kLds, kPhilox>(a, tab, t);
-    if (t >= 128 && t - 128 < a.tail) {
-      const uint64_t k = a.head + 4 * a.nvec + (t - 128);
+  if (blockIdx.x == 0) {  // the elements before the first vector (under 1024) and after the last
+    for (uint64_t k = threadIdx.x; k < a.head; k += kBlock) a.out[k] = choice_elem<kLds, kPhilox>(a, tab, k);
+    if (threadIdx.x < a.tail) {
+      const uint64_t k = a.head + 4 * a.nvec + threadIdx.x;
       a.out[k] = choice_elem<kLds, kPhilox>(a, tab, k);
     }
   }
@@ -223,8 +222,10 @@ static tk_status choice_fill(ChoiceArgs a, uint64_t start_draw, uint64_t n, uint
   if (dev != table->device) return TK_EINVAL;
   a.out = out;
   a.start = start_draw;
-  const uint64_t mis = (uintptr_t)out & 15u;
-  a.head = mis ? (16 - mis) / 4 : 0;
+  // vectors from the output's first 4 KiB boundary, as in the streaming fills: a tile that
+  // spans two 4 KiB blocks stores slower; the elements before it are written singly
+  const uint64_t mis = (uintptr_t)out & 4095u;
+  a.head = mis ? (4096 - mis) / 4 : 0;
   if (a.head > n) a.head = n;
   a.nvec = (n - a.head) / 4;
   a.tail = (uint32_t)(n - a.head - 4 * a.nvec);
