@@ -18,7 +18,8 @@
  *   - Pointers `out`, `x`, `y`, `mask` are device pointers owned by the caller; they must
  *     stay valid until the work enqueued on `stream` has finished.  The library never
  *     keeps them.  `out` must be aligned to its element size; any such alignment is
- *     accepted (16-byte stores are used where the address allows).
+ *     accepted and fills at full speed (16-byte stores from the first 4 KiB boundary of
+ *     `out`, the elements before it one at a time).
  *   - Calls are asynchronous and ordered on `stream` (NULL = the device's null stream)
  *     on the device current to the calling host thread.  Any host thread may call.
  *   - Arguments are checked before anything is enqueued; on any error nothing is
