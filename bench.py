@@ -78,6 +78,7 @@ def build_step(tk, torch, n):
     ]
     # rows beyond the hot path, timed after it and not counted in `value`
     m20, m24 = 1 << 20, 1 << 24
+    mis_n = n - m20
     next_rows = [
         ("exponential_f64", 8 * n, 0, 1, lambda s: tk.tk_fill_exponential_f64(ks(s), st(s), n, optr)),
         ("exponential_f32", 4 * n, 0, 1, lambda s: tk.tk_fill_exponential_f32(ks(s), st(s), n, optr)),
@@ -91,10 +92,12 @@ def build_step(tk, torch, n):
         ("philox_normal_f64", 8 * n, 0, zig_kernels, lambda s: tk.tk_philox_fill_normal_f64(1, st(s), n, optr)),
         ("normal_f32_half_turn", 4 * n, 0, 1, lambda s: tk.tk_fill_normal_f32_half_turn(1, st(s), n, optr)),
         ("randn_f32", 4 * n, 0, 1, lambda s: tk.tk_fill_randn_f32(1, 0, n, optr)),
-        # outputs 8 bytes past a 4 KiB boundary (n - 1 elements, inside the buffer): the
-        # vector grid starts at the next boundary, the head is written element by element
-        ("u32_out+8B", 4 * (n - 1), 0, 1, lambda s: tk.tk_fill_u32(1, 0, n - 1, optr + 8)),
-        ("normal_f64_out+8B", 8 * (n - 1), 0, 2 if zig_kernels == 1 else zig_kernels, lambda s: tk.tk_fill_normal_f64(1, 0, n - 1, optr + 8)),
+        # outputs 8 bytes past a 4 KiB boundary: the vector grid starts at the next boundary
+        # and the head is written element by element (2^28 - 2^20 elements, so that these
+        # launches differ in grid size from the step's in a kernel trace)
+        ("u32_out+8B", 4 * mis_n, 0, 1, lambda s: tk.tk_fill_u32(1, 0, mis_n, optr + 8)),
+        ("normal_f64_out+8B", 8 * mis_n, 0, 2 if zig_kernels == 1 else zig_kernels,
+         lambda s: tk.tk_fill_normal_f64(1, 0, mis_n, optr + 8)),
         # short fills (latency rows: 4 MiB and 8 MiB sit in the caches)
         ("u32_2^20", 4 * m20, 0, 1, lambda s: tk.tk_fill_u32(1, 0, m20, optr)),
         ("normal_f64_2^20", 8 * m20, 0, zig_kernels, lambda s: tk.tk_fill_normal_f64(1, st(s), m20, optr)),
