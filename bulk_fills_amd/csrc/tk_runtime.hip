@@ -82,8 +82,21 @@ static uint32_t g_alloc_skip = 0;  // allocations still to succeed before the fo
 static uint32_t g_alloc_fail = 0;  // forced failures still to come
 static std::atomic<uint64_t> g_device_bytes{0};
 
+// TK_DEBUG_FAIL_ALLOC=<n>: the process's first n device allocations fail.  Read once,
+// before the first allocation or the first tk_debug_fail_allocations call, whichever
+// comes first (a later call replaces it).
+static void apply_env_failures() {
+  static std::once_flag once;
+  std::call_once(once, [] {
+    const uint64_t n = env_u64("TK_DEBUG_FAIL_ALLOC", 0);
+    std::lock_guard<std::mutex> lock(g_alloc_mutex);
+    if (n) g_alloc_fail = n > 0xFFFFFFFFull ? 0xFFFFFFFFu : (uint32_t)n;
+  });
+}
+
 hipError_t device_alloc(void **p, size_t bytes) {
   *p = nullptr;
+  apply_env_failures();
   {
     std::lock_guard<std::mutex> lock(g_alloc_mutex);
     if (g_alloc_skip > 0) {
@@ -141,6 +154,7 @@ const char *tk_status_string(tk_status s) {
 int tk_last_hip_error(void) { return tk::g_last_hip_error; }
 
 tk_status tk_debug_fail_allocations(uint32_t skip, uint32_t count) {
+  tk::apply_env_failures();
   std::lock_guard<std::mutex> lock(tk::g_alloc_mutex);
   tk::g_alloc_skip = count ? skip : 0;
   tk::g_alloc_fail = count;

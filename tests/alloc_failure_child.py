@@ -122,5 +122,23 @@ def main():
     print("alloc_failure_child: ok", flush=True)
 
 
+def env_mode():
+    """Run with TK_DEBUG_FAIL_ALLOC=2: the first two fills fail (each at its first
+    allocation), the third allocates and fills."""
+    n = (1 << 12) + 3
+    out = torch.full((n,), SENTINEL, dtype=torch.float64, device="cuda")
+    for attempt in range(2):
+        log(f"environment: fill {attempt} fails")
+        expect_enomem(lambda: tk.tk_fill_normal_f64(5, 0, n, out), f"environment, fill {attempt}")
+        assert tk.tk_debug_device_bytes() == 0
+        untouched(out, f"environment, fill {attempt}")
+    tk.tk_fill_normal_f64(5, 0, n, out)
+    torch.cuda.synchronize()
+    want, path = oracle.fill_normal_f64(5, 0, n, with_path=True)
+    check_normal(out, want, path, "environment, third fill")
+    print("alloc_failure_child: ok", flush=True)
+
+
 if __name__ == "__main__":
-    main()
+    import sys
+    env_mode() if sys.argv[1:] == ["env"] else main()

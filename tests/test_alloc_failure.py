@@ -26,13 +26,27 @@ def test_hook_arguments():
     tk.tk_debug_fail_allocations(0, 0)
 
 
+def run_child(args, extra_env=None):
+    env = dict(os.environ)
+    env.pop("TK_DEBUG_FAIL_ALLOC", None)
+    env.update(extra_env or {})
+    env["PYTHONPATH"] = os.pathsep.join([ROOT, HERE] + [p for p in [env.get("PYTHONPATH")] if p])
+    print("alloc_failure_child.py", *args, flush=True)
+    return subprocess.run([sys.executable, "-u", os.path.join(HERE, "alloc_failure_child.py")] + args, cwd=ROOT,
+                          env=env, capture_output=True, text=True, timeout=110)
+
+
+@pytest.mark.gpu
+def test_failures_from_the_environment():
+    r = run_child(["env"], {"TK_DEBUG_FAIL_ALLOC": "2"})
+    print(r.stdout[-4000:], r.stderr[-4000:], flush=True)
+    assert r.returncode == 0, f"exit status {r.returncode}"
+    assert "alloc_failure_child: ok" in r.stdout
+
+
 @pytest.mark.gpu
 def test_forced_failures_in_a_fresh_process():
-    env = dict(os.environ)
-    env["PYTHONPATH"] = os.pathsep.join([ROOT, HERE] + [p for p in [env.get("PYTHONPATH")] if p])
-    print("alloc_failure_child.py", flush=True)
-    r = subprocess.run([sys.executable, "-u", os.path.join(HERE, "alloc_failure_child.py")], cwd=ROOT, env=env,
-                       capture_output=True, text=True, timeout=110)
+    r = run_child([])
     print(r.stdout[-4000:], r.stderr[-4000:], flush=True)
     assert r.returncode == 0, f"exit status {r.returncode}"
     assert "alloc_failure_child: ok" in r.stdout
