@@ -8,10 +8,14 @@ int64 with a low bound), the f64 ziggurat and f32 Box-Muller normals, fused drop
 X = f32[2^20, 256] (p = 0.1), the choice fill through a 1000-way Zipf(1.1) alias table,
 and the Philox4x32-10 u32 fill.  Inputs are resident in device memory before timing.
 
-The JSON line reports the whole step's bytes written per second (`value`), each fill's
-median rate, the roofline of the dominant kernel (algorithmic bytes per launch over its
-HIP-event-timed average duration, against the 8 TB/s HBM peak), and the CPU oracle timed
-on a bounded sample of the same step on this host.
+The JSON line reports the whole step's bytes written per second (`value`); each fill's
+median and fastest of 21 event-timed launches after 2 s of warm-up per row (tandem-cuda,
+"Performance", §GPU: 2 s of warm-up, the median of 21 fills, the fastest within a few
+percent), as GiB/s and as a fraction of the 8 TB/s HBM peak and of the measured store
+ceiling (the library's constant fill, which has the fills' store path and no generator,
+and hipMemsetAsync, at each output size); per-start rows; the roofline of the dominant
+kernel (algorithmic bytes per launch over its HIP-event-timed average duration); and the
+CPU oracle timed on this host's cores over the same step.
 """
 import argparse
 import json
@@ -24,17 +28,24 @@ import numpy as np
 
 GIB = float(1 << 30)
 HBM_PEAK_GBS = 8000.0
+# dependent integer steps per lane before each store of the constant fill, swept for the
+# store ceiling (stores spaced by some arithmetic, as in the fills, can go faster than
+# stores issued back to back)
+CONST_WORK = (0, 8, 16, 32, 64, 128)
 
 
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--warmup-seconds", type=float, default=2.0,
-                    help="keep warming up for at least this long (the pages warm each row for 2 s)")
-    ap.add_argument("--cpu-sample-log2", type=int, default=27,
-                    help="elements per fill in the oracle's CPU sample (0 disables it)")
+    ap.add_argument("--warmup", type=int, default=5, help="untimed steps before the timed ones")
+    ap.add_argument("--row-warmup-seconds", type=float, default=2.0,
+                    help="warm-up of each hot-path row before its 21 timed launches (the pages warm each "
+                         "row for 2 s); rows outside the step get a quarter of it")
+    ap.add_argument("--row-launches", type=int, default=21, help="timed launches per row")
+    ap.add_argument("--cpu-single-log2", type=int, default=26,
+                    help="elements per fill in the one-core oracle sample (0: skip it)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--only", default="",
                     help="comma-separated fill names to run (profiling); 'calib_copy' adds a plain 1 GiB "
                          "device copy used to calibrate the HBM byte counters")
@@ -42,7 +53,9 @@ def parse():
 
 
 def build_step(tk, torch, n):
-    """Returns a list of (name, bytes_written, bytes_read, kernels, fn(step_index))."""
+    """Returns the step's fills and the rows outside it, each (name, bytes_written,
+    bytes_read, kernels, fn(step_index)); the per-start rows and the store-ceiling rows;
+    and the buffers they use."""
     import tk_inputs as ti
     dev = torch.device("cuda")
     out = torch.empty(8 * n, dtype=torch.uint8, device=dev)   # 2 GiB, reused by every fill
@@ -106,7 +119,48 @@ def build_step(tk, torch, n):
     # not a fill: a plain copy of a known size, only when named with --only
     xc = x.view(torch.uint8)
     calib = ("calib_copy", 4 * n, 4 * n, 1, lambda s: out[:4 * n].copy_(xc))
-    return fills, next_rows, calib, (out, x, table)
+
+    # one row per start draw: (fill, start, bytes written, fn)
+    def at(fill, nb, f):
+        return [(fill, s0, nb, (lambda s0: lambda s: f(s0))(s0)) for s0 in starts[fill]]
+    starts = {"normal_f64": (0, 1, 3), "normal_f64_2^24": (0, 1, 3), "philox_u32": (0, 1, 2, 3),
+              "normal_f32": (0, 1, 3), "normal_f32_half_turn": (0, 1), "u16": (0, 1), "f16_bits": (0, 1),
+              "u8": (0, 1, 3), "philox_normal_f32": (0, 1, 2, 3)}
+    start_rows = (at("normal_f64", 8 * n, lambda s0: tk.tk_fill_normal_f64(1, s0, n, optr))
+                  + at("normal_f64_2^24", 8 * m24, lambda s0: tk.tk_fill_normal_f64(1, s0, m24, optr))
+                  + at("philox_u32", 4 * n, lambda s0: tk.tk_philox_fill_u32(1, s0, n, optr))
+                  + at("normal_f32", 4 * n, lambda s0: tk.tk_fill_normal_f32(1, s0, n, optr))
+                  + at("normal_f32_half_turn", 4 * n, lambda s0: tk.tk_fill_normal_f32_half_turn(1, s0, n, optr))
+                  + at("u16", 2 * n, lambda s0: tk.tk_fill_u16(1, s0, n, optr))
+                  + at("f16_bits", 2 * n, lambda s0: tk.tk_fill_f16_bits(1, s0, n, optr))
+                  + at("u8", n, lambda s0: tk.tk_fill_u8(1, s0, n, optr))
+                  + at("philox_normal_f32", 4 * n, lambda s0: tk.tk_philox_fill_normal_f32(1, s0, n, optr)))
+
+    # the store ceiling at every output size of the step: the library's constant fill (the
+    # fills' own store path, no generator) and the runtime's hipMemsetAsync
+    import ctypes as C
+    hip = tk.lib
+    hip.hipMemsetAsync.argtypes = [C.c_void_p, C.c_int, C.c_size_t, C.c_void_p]
+    hip.hipMemsetAsync.restype = C.c_int
+
+    def memset(nb):
+        rc = hip.hipMemsetAsync(optr, 0, nb, torch.cuda.current_stream().cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"hipMemsetAsync failed: hipError {rc}")
+    def const_fill(nb, work):
+        def f(s):
+            tk.tk_debug_set_tunable("const_work", work)
+            try:
+                tk.tk_fill_constant_u32(0, nb // 4, optr)
+            finally:
+                tk.tk_debug_set_tunable("const_work", -1)
+        return f
+    ceil_rows = []
+    for nb in (n, 2 * n, 4 * n, 8 * n):
+        for work in CONST_WORK:
+            ceil_rows.append((f"constant_fill_work{work}", nb, const_fill(nb, work)))
+        ceil_rows.append(("hipMemsetAsync", nb, (lambda nb: lambda s: memset(nb))(nb)))
+    return fills, next_rows, calib, start_rows, ceil_rows, (out, x, table)
 
 
 class FenceFreeEvent:
@@ -171,37 +225,84 @@ def measured_traffic(fill):
     return rec["traffic_bytes"] if h.hexdigest() == rec["source_sha256"] else None
 
 
-def cpu_baseline(n_sample):
-    """The oracle (single-threaded C) over the same fills at n_sample elements each."""
+def _oracle_jobs(x):
+    """(bytes written per element, fn(start, n)) for every fill of one step, over the oracle.
+    x: the dropout input of at least as many elements as the largest call."""
     import oracle
     import tk_inputs as ti
-    x = ti.normal_x(n_sample)
     q, a, _ = oracle.alias_build(ti.zipf_weights())
-    m = n_sample
-    jobs = [
-        (4 * m, lambda: oracle.fill_u32(1, 0, m)), (8 * m, lambda: oracle.fill_u64(1, 0, m)),
-        (4 * m, lambda: oracle.fill_f32(1, 0, m)), (8 * m, lambda: oracle.fill_f64(1, 0, m)),
-        (2 * m, lambda: oracle.fill_u16(1, 0, m)), (2 * m, lambda: oracle.fill_f16_bits(1, 0, m)),
-        (m, lambda: oracle.fill_u8(1, 0, m)), (m, lambda: oracle.fill_bool(1, 0, m)),
-        (4 * m, lambda: oracle.fill_u32_below(1, 0, m, 1000)),
-        (4 * m, lambda: oracle.fill_u32_below(1, 0, m, (1 << 32) - 2)),
-        (8 * m, lambda: oracle.fill_u64_below(1, 0, m, 1000)),
-        (8 * m, lambda: oracle.fill_u64_below(1, 0, m, (1 << 64) - 2)),
-        (4 * m, lambda: oracle.fill_i32_below(1, 0, m, ti.LOW, ti.LOW_BOUND)),
-        (8 * m, lambda: oracle.fill_i64_below32(1, 0, m, ti.LOW, ti.LOW_BOUND)),
-        (8 * m, lambda: oracle.fill_normal_f64(1, 0, m)), (4 * m, lambda: oracle.fill_normal_f32(1, 0, m)),
-        (4 * m, lambda: oracle.dropout_f32(ti.DROPOUT_KEY, 0, x, ti.DROPOUT_P, with_mask=False)),
-        (4 * m, lambda: oracle.fill_choice_u32(1, 0, m, q, a)), (4 * m, lambda: oracle.philox_fill_u32(1, 0, m)),
+    L, LB = ti.LOW, ti.LOW_BOUND
+    return [
+        (4, lambda s, m: oracle.fill_u32(1, s, m)), (8, lambda s, m: oracle.fill_u64(1, s, m)),
+        (4, lambda s, m: oracle.fill_f32(1, s, m)), (8, lambda s, m: oracle.fill_f64(1, s, m)),
+        (2, lambda s, m: oracle.fill_u16(1, s, m)), (2, lambda s, m: oracle.fill_f16_bits(1, s, m)),
+        (1, lambda s, m: oracle.fill_u8(1, s, m)), (1, lambda s, m: oracle.fill_bool(1, s, m)),
+        (4, lambda s, m: oracle.fill_u32_below(1, s, m, 1000)),
+        (4, lambda s, m: oracle.fill_u32_below(1, s, m, (1 << 32) - 2)),
+        (8, lambda s, m: oracle.fill_u64_below(1, s, m, 1000)),
+        (8, lambda s, m: oracle.fill_u64_below(1, s, m, (1 << 64) - 2)),
+        (4, lambda s, m: oracle.fill_i32_below(1, s, m, L, LB)),
+        (8, lambda s, m: oracle.fill_i64_below32(1, s, m, L, LB)),
+        (8, lambda s, m: oracle.fill_normal_f64(1, s, m)), (4, lambda s, m: oracle.fill_normal_f32(1, s, m)),
+        (4, lambda s, m: oracle.dropout_f32(ti.DROPOUT_KEY, s, x[s:s + m], ti.DROPOUT_P, with_mask=False)),
+        (4, lambda s, m: oracle.fill_choice_u32(1, s, m, q, a)), (4, lambda s, m: oracle.philox_fill_u32(1, s, m)),
     ]
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def host_threads():
+    """Threads for the all-core oracle run: the CPUs this process may use, at most 16 (one
+    GPU's share of the host)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def cpu_baseline(n_full, single_log2):
+    """The oracle (plain single-threaded C, untouched) over every fill of one step.
+    All cores: each fill at the full n_full elements, cut into P contiguous ranges run on P
+    threads at once (a fill cut at any element equals the whole fill; ctypes releases the
+    GIL during each call).  One core: each fill at 2^single_log2 elements, one call."""
+    import tk_inputs as ti
+    from concurrent.futures import ThreadPoolExecutor
+    P = host_threads()
+    x = ti.normal_x(n_full)
+    jobs = _oracle_jobs(x)
+    cut = [(n_full * j) // P for j in range(P + 1)]
     total_bytes, total_s = 0, 0.0
-    for nbytes, fn in jobs:
-        t0 = time.perf_counter()
-        fn()
-        total_s += time.perf_counter() - t0
-        total_bytes += nbytes
-    return {"value": total_bytes / total_s / GIB, "unit": "GiB/s", "cores": 1, "kind": "oracle",
-            "sample": f"every fill of one step at 2^{int(np.log2(n_sample))} elements instead of 2^28 "
-                      f"(single-threaded C oracle, {total_s:.1f} s)"}
+    with ThreadPoolExecutor(P) as pool:
+        for nb, fn in jobs:
+            t0 = time.perf_counter()
+            list(pool.map(lambda j: fn(cut[j], cut[j + 1] - cut[j]) is None, range(P)))
+            total_s += time.perf_counter() - t0
+            total_bytes += nb * n_full
+    rec = {"value": round(total_bytes / total_s / GIB, 3), "unit": "GiB/s", "cores": P, "kind": "oracle",
+           "sample": f"every fill of one step at the full 2^{int(np.log2(n_full))} elements, each cut into {P} "
+                     f"contiguous ranges on {P} threads ({total_s:.1f} s wall)",
+           "cpu_model": cpu_model(), "host_cpus": os.cpu_count()}
+    if single_log2 > 0:
+        m = 1 << single_log2
+        b1, s1 = 0, 0.0
+        for nb, fn in jobs:
+            t0 = time.perf_counter()
+            fn(0, m)
+            s1 += time.perf_counter() - t0
+            b1 += nb * m
+        rec["single_core"] = {"value": round(b1 / s1 / GIB, 3), "unit": "GiB/s", "cores": 1,
+                              "sample": f"every fill of one step at 2^{single_log2} elements, one thread "
+                                        f"({s1:.1f} s)"}
+    return rec
 
 
 def device_info():
@@ -218,6 +319,49 @@ def device_info():
             "hip_runtime_version": hip_rt, "torch": torch.__version__, "torch_hip": torch.version.hip}
 
 
+class RowTimer:
+    """Times launches of one row: a warm-up of at least `warm_s` seconds, then `k` launches
+    each between a pair of fence-free events recorded on the launch stream (back to back:
+    no synchronisation between them), then the same k launches between a single pair."""
+
+    def __init__(self, tk, torch, k):
+        self.tk, self.torch, self.k = tk, torch, k
+        self.ev = [(FenceFreeEvent(tk.lib), FenceFreeEvent(tk.lib)) for _ in range(k)]
+        self.batch = (FenceFreeEvent(tk.lib), FenceFreeEvent(tk.lib))
+
+    def time(self, fn, warm_s):
+        torch = self.torch
+        t_end = time.perf_counter() + warm_s
+        w = 0
+        while True:
+            fn(w)
+            w += 1
+            if w % 8 == 0:
+                torch.cuda.synchronize()
+                if time.perf_counter() >= t_end:
+                    break
+        for s, (a, b) in enumerate(self.ev):
+            a.record()
+            fn(s)
+            b.record()
+        self.batch[0].record()
+        for s in range(self.k):
+            fn(s)
+        self.batch[1].record()
+        torch.cuda.synchronize()
+        ms = sorted(a.elapsed_time(b) for a, b in self.ev)
+        return {"median_ms": statistics.median(ms), "min_ms": ms[0], "max_ms": ms[-1],
+                "batched_ms": self.batch[0].elapsed_time(self.batch[1]) / self.k, "warmup_launches": w}
+
+
+def progress(msg):
+    print(f"bench: {msg}", file=sys.stderr, flush=True)
+
+
+def rate(nbytes, ms):
+    return nbytes / (ms / 1e3) / GIB
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -229,11 +373,11 @@ def main():
     import tk_inputs as ti
 
     n = ti.FULL_N
-    fills, next_rows, calib, keep = build_step(tk, torch, n)
+    fills, next_rows, calib, start_rows, ceil_rows, keep = build_step(tk, torch, n)
     if args.only:
         wanted = set(args.only.split(","))
         fills = [f for f in fills + next_rows + [calib] if f[0] in wanted]
-        next_rows = []
+        next_rows, start_rows, ceil_rows = [], [], []
     torch.cuda.synchronize()
 
     def step(s, events=None):
@@ -246,47 +390,59 @@ def main():
             if ev is not None:
                 ev[1].record()
 
-    t_end = time.perf_counter() + args.warmup_seconds
-    w = 0
-    while w < args.warmup or time.perf_counter() < t_end:
+    # warm-up: exactly W untimed steps
+    for w in range(args.warmup):
         step(w)
-        w += 1
-        if w % 10 == 0:
-            torch.cuda.synchronize()
     torch.cuda.synchronize()
 
     K = args.steps
+    R = args.row_launches
     bytes_step = sum(f[1] for f in fills)
+    rt = RowTimer(tk, torch, R)
+    warm = args.row_warmup_seconds
 
-    def pairs():
-        return (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    # store ceiling first, so that every fill can be set against it
+    ceiling = {}
+    for name, nb, fn in ceil_rows:
+        t = rt.time(fn, warm / 4)
+        progress(f"ceiling {name} {nb >> 20} MiB: {t['median_ms'] * 1e3:.1f} us")
+        ceiling.setdefault(name, {})[str(nb)] = {
+            "GiB_per_s": round(rate(nb, t["median_ms"]), 1), "GiB_per_s_fastest": round(rate(nb, t["min_ms"]), 1),
+            "median_us": round(t["median_ms"] * 1e3, 2), "min_us": round(t["min_ms"] * 1e3, 2)}
 
-    # per-fill pass, outside the timed region: an event pair around every fill of K steps
-    evs = [{j: pairs() for j in range(len(fills))} for _ in range(K)]
-    for s in range(K):
-        step(s, evs[s])
-    torch.cuda.synchronize()
-    # and each fill K times back to back between one event pair (no event records between
-    # its launches): the sustained time per fill, the figure its GiB/s is quoted on
-    batch = []
-    for j, f in enumerate(fills):
-        a, b = pairs()
-        a.record()
-        for s in range(K):
-            f[4](s)
-        b.record()
-        batch.append((a, b))
-    torch.cuda.synchronize()
+    def ceiling_at(nb):
+        c = [ceiling[k][str(nb)]["GiB_per_s"] for k in ceiling if str(nb) in ceiling[k]]
+        return max(c) if c else None
+
+    # per output size: the fastest store-only kernel (median of its launches) and which it was
+    ceiling_best = {}
+    for k, per in ceiling.items():
+        for nb, r in per.items():
+            if nb not in ceiling_best or r["GiB_per_s"] > ceiling_best[nb]["GiB_per_s"]:
+                ceiling_best[nb] = {"GiB_per_s": r["GiB_per_s"], "kernel": k,
+                                    "pct_of_hbm_peak": round(100 * r["GiB_per_s"] * GIB / 1e9 / HBM_PEAK_GBS, 2)}
+
+    def row_record(nb, rbytes, t):
+        rec = {"GiB_per_s": round(rate(nb, t["median_ms"]), 1),
+               "GiB_per_s_fastest": round(rate(nb, t["min_ms"]), 1),
+               "median_us": round(t["median_ms"] * 1e3, 2), "min_us": round(t["min_ms"] * 1e3, 2),
+               "batched_us": round(t["batched_ms"] * 1e3, 2),
+               "pct_of_hbm_peak": round(100 * (nb + rbytes) / (t["median_ms"] / 1e3) / 1e9 / HBM_PEAK_GBS, 2)}
+        c = ceiling_at(nb)
+        if c and not rbytes:
+            rec["pct_of_store_ceiling"] = round(100 * rec["GiB_per_s"] / c, 2)
+        return rec
+
+    # per-fill pass, outside the timed region: warm-up, then 21 event-timed launches per row
     per_fill = {}
-    for j, (name, wbytes, rbytes, nk, _) in enumerate(fills):
-        ms = [evs[s][j][0].elapsed_time(evs[s][j][1]) for s in range(K)]
-        per_launch = batch[j][0].elapsed_time(batch[j][1]) / K
-        per_fill[name] = {"median_ms": statistics.median(ms), "mean_ms": statistics.fmean(ms),
-                          "batched_ms": per_launch, "GiB_per_s": wbytes / (per_launch / 1e3) / GIB,
-                          "bytes_written": wbytes, "bytes_read": rbytes, "kernels": nk}
+    for name, wbytes, rbytes, nk, fn in fills:
+        t = rt.time(fn, warm)
+        progress(f"{name}: {t['median_ms'] * 1e3:.1f} us")
+        per_fill[name] = dict(row_record(wbytes, rbytes, t), bytes_written=wbytes, bytes_read=rbytes, kernels=nk,
+                              _median_ms=t["median_ms"])
     # dominant single-kernel fill: the largest share of the step's device time
     single = {k: v for k, v in per_fill.items() if v["kernels"] == 1 and k != "calib_copy"}
-    dom = max(single, key=lambda k: single[k]["mean_ms"])
+    dom = max(single, key=lambda k: single[k]["_median_ms"])
     dj = [f[0] for f in fills].index(dom)
 
     # timed region: K steps; the only instrumentation is an event pair around the dominant
@@ -311,29 +467,31 @@ def main():
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": round(traffic) if traffic is not None else None,
                 "bytes_per_launch": algo_bytes, "avg_launch_ms": round(dom_ms, 5)}
-    # rows beyond the hot path: same protocol, separate loop
-    # (back to back as in the step: an event pair around each launch, one sync at the end)
-    nxt = {}
-    for name, wbytes, _, _, fn in next_rows:
-        for s in range(3):
-            fn(s)
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
-        for s in range(K):
-            ev[s][0].record()
-            fn(s)
-            ev[s][1].record()
-        torch.cuda.synchronize()
-        ms = [a.elapsed_time(b) for a, b in ev]
-        med = statistics.median(ms)
-        nxt[name] = {"GiB_per_s": round(wbytes / (med / 1e3) / GIB, 1), "median_ms": round(med, 4),
-                     "median_us": round(med * 1e3, 1)}
-    cpu = cpu_baseline(1 << args.cpu_sample_log2) if args.cpu_sample_log2 > 0 else None
+    c_dom = ceiling_at(d["bytes_written"])
+    if c_dom:
+        roofline["frac_of_store_ceiling"] = round(algo_bytes / (dom_ms / 1e3) / GIB / c_dom, 4)
 
+    # rows beyond the hot path and per-start rows: same protocol, a shorter warm-up
+    progress(f"timed steps: {elapsed / K * 1e3:.3f} ms per step")
+    nxt = {}
+    for name, wbytes, rbytes, _, fn in next_rows:
+        nxt[name] = row_record(wbytes, rbytes, rt.time(fn, warm / 4))
+        progress(f"{name}: {nxt[name]['median_us']} us")
+    per_start = {}
+    for fill, s0, nb, fn in start_rows:
+        per_start.setdefault(fill, {})[str(s0)] = r = row_record(nb, 0, rt.time(fn, warm / 4))
+        progress(f"{fill} start {s0}: {r['median_us']} us")
+
+    progress("CPU oracle baseline")
+    cpu = None if args.no_cpu else cpu_baseline(n, args.cpu_single_log2)
+
+    for v in per_fill.values():
+        del v["_median_ms"]
     rec = {
         "metric": "GiB/s written per fill (2^28 elems) on 1 MI355X; % of HBM write peak",
-        "value": round(value, 2), "unit": "GiB/s", "n_gpus": 1, "steps": K, "warmup": w,
+        "value": round(value, 2), "unit": "GiB/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
         "ms_per_step": round(elapsed / K * 1e3, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "u32", "data": "synthetic",
+        "vs_baseline": None, "dtype": "per fill: u8/u16/u32/u64 integers, f16/f32/f64", "data": "synthetic",
         "config": {"workload": "every hot-path fill once per step at 2^28 elements: uniform u8/u16/f16/u32/u64/"
                                "f32/f64/bool, bounded (Lemire) x6, ziggurat f64 normal, Box-Muller f32 normal, "
                                "dropout over f32[2^20,256], Zipf(1.1)x1000 choice, Philox u32",
@@ -341,8 +499,12 @@ def main():
         "pct_of_hbm_peak": round(100 * value * GIB / 1e9 / HBM_PEAK_GBS, 2),
         "roofline": roofline,
         "cpu_baseline": cpu,
-        "fills": {k: {"GiB_per_s": round(v["GiB_per_s"], 1), "batched_ms": round(v["batched_ms"], 4),
-                      "event_pair_median_ms": round(v["median_ms"], 4)} for k, v in per_fill.items()},
+        "protocol": {"warmup_steps": args.warmup, "row_warmup_s": warm, "row_warmup_s_outside_step": warm / 4,
+                     "row_launches": R, "row_statistic": "median and fastest of the row launches, each between "
+                     "fence-free HIP events; batched_us = the same launches back to back between one pair"},
+        "store_ceiling": {"best": ceiling_best, "rows": ceiling},
+        "fills": per_fill,
+        "per_start": per_start,
         "next_rows": nxt,
         "device": device_info(),
     }

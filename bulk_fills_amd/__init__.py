@@ -81,6 +81,7 @@ SIGNATURES = {
     "tk_debug_set_tunable": [C.c_char_p, _i64],
     "tk_debug_fail_allocations": [_u32, _u32],
     "tk_debug_device_bytes": [_p],
+    "tk_fill_constant_u32": [_u32, _u64, _p, _p],
 }
 for _name, _args in SIGNATURES.items():
     _fn = getattr(lib, _name)
@@ -168,6 +169,11 @@ tk_philox_fill_f32 = _fill("tk_philox_fill_f32", 4)
 tk_philox_fill_f64 = _fill("tk_philox_fill_f64", 8)
 tk_philox_fill_normal_f32 = _fill("tk_philox_fill_normal_f32", 4)
 tk_philox_fill_normal_f64 = _fill("tk_philox_fill_normal_f64", 8)
+
+
+def tk_fill_constant_u32(value, n, out, stream=None):
+    _check(lib.tk_fill_constant_u32(value, n, _buf(out, 4, n, "tk_fill_constant_u32"), _stream(stream, out)),
+           "tk_fill_constant_u32")
 
 
 def tk_philox_fill_u32_below(key, start_draw, n, bound, out, stream=None):
@@ -287,7 +293,8 @@ def tk_debug_set_normal_f64_mode(mode):
     _check(lib.tk_debug_set_normal_f64_mode(mode), "tk_debug_set_normal_f64_mode")
 
 
-TUNABLES = ("store_nt", "max_blocks", "unroll", "choice_tiles", "exp_tiles", "zig_tiles", "zig_lds", "zig_fused")
+TUNABLES = ("store_nt", "max_blocks", "unroll", "choice_tiles", "exp_tiles", "zig_tiles", "zig_lds", "zig_fused",
+            "const_work")
 
 
 def tk_debug_set_tunable(name, value):

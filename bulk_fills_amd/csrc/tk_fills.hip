@@ -163,6 +163,28 @@ __device__ __forceinline__ uint32_t lo32(uint64_t x) { return (uint32_t)x; }
 __device__ __forceinline__ uint32_t hi32(uint64_t x) { return (uint32_t)(x >> 32); }
 
 // ---------------------------------------------------------------------------------------
+// Constant fill: no generator, only the store path.  The same geometry, grid and 16-byte
+// stores as every streaming fill, so its rate is the ceiling those fills are measured
+// against.
+// ---------------------------------------------------------------------------------------
+// `work` (a tunable, 0 by default) puts a chain of that many dependent integer steps before
+// each lane's store: the fills store after some arithmetic, and the rate of stores spaced
+// that way is part of what the ceiling has to cover.
+struct OpConst : FillBase<uint32_t> {
+  uint32_t value;
+  uint32_t work;
+  __device__ __forceinline__ uint32_t elem(uint64_t) const { return value; }
+  __device__ __forceinline__ uint4 vec(uint64_t v) const {
+    if (work) {
+      uint32_t x = (uint32_t)v;
+      for (uint32_t i = 0; i < work; ++i) x = x * 0x01000193u + i;
+      __asm__ volatile("" ::"v"(x));  // keeps the chain; the stored value does not depend on it
+    }
+    return u4(value, value, value, value);
+  }
+};
+
+// ---------------------------------------------------------------------------------------
 // Uniform fills
 // ---------------------------------------------------------------------------------------
 // u32 / f32: draw i is word i.
@@ -373,6 +395,9 @@ struct OpRandnF32 : FillBase<float> {
 // ---------------------------------------------------------------------------------------
 // f64: u = (d & (2^53 - 1)) 2^-53 of the 64-bit draw.
 struct OpExpF64 : FillBase<uint64_t> {
+  using Entry = LogEntry;
+  static constexpr int kEntries = TK_LOG_ENTRIES;
+  __device__ static const Entry *table() { return kLogTable; }
   uint32_t hk;
   __device__ __forceinline__ uint64_t one(uint32_t lo, uint32_t hi, const LogEntry *tab) const {
     return (uint64_t)__double_as_longlong(neg_ln_unit(1.0 - unit53_lowbits(lo, hi), tab));
@@ -390,25 +415,29 @@ struct OpExpF64 : FillBase<uint64_t> {
 
 // f32: u = (w & 0xFFFFFF) 2^-24.
 struct OpExpF32 : FillBase<uint32_t> {
+  using Entry = LogEntryF;
+  static constexpr int kEntries = TK_LOGF_ENTRIES;
+  __device__ static const Entry *table() { return kLogTableF; }
   uint32_t hk;
-  __device__ __forceinline__ uint32_t one(uint32_t w, const LogEntry *tab) const {
-    return __float_as_uint(neg_ln_grid24_f32(1.0 - (double)(w & 0xFFFFFFu) * 0x1p-24, tab));
+  __device__ __forceinline__ uint32_t one(uint32_t w, const LogEntryF *tab) const {
+    return __float_as_uint(neg_ln_grid24_f32(w & 0xFFFFFFu, tab));
   }
-  __device__ __forceinline__ uint32_t elem(uint64_t k) const { return one(word(hk, (uint32_t)(start + k)), kLogTable); }
-  __device__ __forceinline__ uint4 vec(uint64_t v, const LogEntry *tab) const {
+  __device__ __forceinline__ uint32_t elem(uint64_t k) const { return one(word(hk, (uint32_t)(start + k)), kLogTableF); }
+  __device__ __forceinline__ uint4 vec(uint64_t v, const LogEntryF *tab) const {
     const uint32_t c = (uint32_t)vec_draw(v);
     return u4(one(word(hk, c), tab), one(word(hk, c + 1), tab), one(word(hk, c + 2), tab), one(word(hk, c + 3), tab));
   }
 };
 
-// Exponential fills: T 4 KiB tiles per work-group after copying the 4 KiB logarithm table
-// to LDS (one 16-byte load per thread), so the per-element table reads are ds_reads and
-// not L1 gathers through the texture addresser.
+// Exponential fills: T 4 KiB tiles per work-group after copying the fill's 4 KiB logarithm
+// table to LDS (one 16-byte load per thread), so the per-element table reads are ds_reads
+// and not L1 gathers through the texture addresser.
 template <class Op, int T, bool kNT>
 __global__ __launch_bounds__(kBlock) void k_exp_fill(Op op) {
-  static_assert(sizeof(LogEntry) * TK_LOG_ENTRIES == 16 * kBlock, "one 16-byte piece of the table per thread");
-  __shared__ LogEntry tab[TK_LOG_ENTRIES];
-  ((uint4 *)tab)[threadIdx.x] = ((const uint4 *)kLogTable)[threadIdx.x];
+  using Entry = typename Op::Entry;
+  static_assert(sizeof(Entry) * Op::kEntries == 16 * kBlock, "one 16-byte piece of the table per thread");
+  __shared__ Entry tab[Op::kEntries];
+  ((uint4 *)tab)[threadIdx.x] = ((const uint4 *)Op::table())[threadIdx.x];
   __syncthreads();
   const uint64_t v0 = (uint64_t)blockIdx.x * T * kBlock + threadIdx.x;
 #pragma unroll
@@ -660,6 +689,16 @@ static tk_status below64(uint32_t key, uint64_t start_draw, uint64_t n, int64_t 
 }  // namespace
 
 extern "C" {
+
+tk_status tk_fill_constant_u32(uint32_t value, uint64_t n, uint32_t *out, hipStream_t stream) {
+  if (n == 0) return TK_OK;
+  if (!out || !elem_aligned(out)) return TK_EINVAL;
+  if (n > (~0ull >> 2)) return TK_ERANGE;  // n * 4 bytes must be addressable
+  OpConst op{};
+  op.value = value;
+  op.work = (uint32_t)config().const_work;
+  return run_simple(op, out, 0, n, stream);
+}
 
 tk_status tk_fill_u32(uint32_t key, uint64_t start_draw, uint64_t n, uint32_t *out, hipStream_t stream) {
   TK_PRECHECK(out, kMaxW32);

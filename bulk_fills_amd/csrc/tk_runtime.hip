@@ -42,14 +42,17 @@ static bool env_tunable(Config &c, const char *name) {
   } else if (!strcmp(name, "zig_fused")) {
     const char *zm = getenv("TK_ZIG_MODE");
     c.zig_fused = !(zm && strcmp(zm, "split") == 0);
+  } else if (!strcmp(name, "const_work")) {
+    const uint64_t w = env_u64("TK_CONST_WORK", 0);
+    c.const_work = w > 4096 ? 4096 : (int)w;
   } else {
     return false;
   }
   return true;
 }
 
-static const char *const kTunables[] = {"store_nt",  "max_blocks", "unroll",  "choice_tiles",
-                                        "exp_tiles", "zig_tiles",  "zig_lds", "zig_fused"};
+static const char *const kTunables[] = {"store_nt",  "max_blocks", "unroll",  "choice_tiles", "exp_tiles",
+                                        "zig_tiles", "zig_lds",    "zig_fused", "const_work"};
 
 static Config &mutable_config() {
   static Config cfg;
@@ -185,6 +188,7 @@ tk_status tk_debug_set_tunable(const char *name, int64_t value) {
   else if (!strcmp(name, "zig_tiles") && one_of({1, 2, 4, 8, 16})) c.zig_tiles = (int)value;
   else if (!strcmp(name, "zig_lds") && one_of({0, 1})) c.zig_lds = value == 1;
   else if (!strcmp(name, "zig_fused") && one_of({0, 1})) c.zig_fused = value == 1;
+  else if (!strcmp(name, "const_work") && value <= 4096) c.const_work = (int)value;
   else return TK_EINVAL;
   return TK_OK;
 }

@@ -203,6 +203,15 @@ tk_status tk_philox_fill_choice_u32(uint64_t key, uint64_t start_draw, uint64_t 
 tk_status tk_philox_fill_normal_f32(uint64_t key, uint64_t start_draw, uint64_t n, float *out, hipStream_t stream);
 tk_status tk_philox_fill_normal_f64(uint64_t key, uint64_t start_draw, uint64_t n, double *out, hipStream_t stream);
 
+/* ---- Store ceiling ------------------------------------------------------------------
+ * The store path alone: out[k] = value for k < n, written with exactly the streaming
+ * fills' geometry, grid and 16-byte stores and no generator.  The rate at which the device
+ * takes this kernel's stores is the measured ceiling the fills are reported against (the
+ * pages' fills run at ~95 % of their GPU's bandwidth: tandem-cuda, "Performance", §GPU and
+ * the notes under its table).  out must be 4-byte aligned; n * 4 must fit 64 bits, else
+ * TK_ERANGE.                                                                            */
+tk_status tk_fill_constant_u32(uint32_t value, uint64_t n, uint32_t *out, hipStream_t stream);
+
 /* ---- Status and introspection -------------------------------------------------------*/
 const char *tk_status_string(tk_status status);
 /* The hipError_t of the last TK_EHIP returned to the calling thread (0 if none). */
@@ -253,6 +262,9 @@ tk_status tk_debug_device_bytes(uint64_t *bytes);
  *   "zig_lds" 0|1         ziggurat layer gathers from an LDS copy or from L1/L2 (TK_ZIG_TABLE)
  *   "zig_fused" 0|1       ziggurat misses finished in the table pass or a second kernel
  *                         (TK_ZIG_MODE; tk_debug_set_normal_f64_mode overrides it)
+ *   "const_work" 0..4096  dependent integer steps per lane before each store of
+ *                         tk_fill_constant_u32 (TK_CONST_WORK; 0 = none): the spacing of
+ *                         the store-ceiling measurement
  * A negative value restores the environment's setting.  Unknown names or values: TK_EINVAL.
  * Not synchronized with launches in flight on other threads beyond each value being read
  * atomically. */

@@ -128,6 +128,13 @@ def test_philox_variant_validation():
     assert L.tk_philox_fill_choice_u32(1, 0, 4, None, FAKE, None) == tk.TK_EINVAL
 
 
+def test_constant_fill_validation():
+    assert L.tk_fill_constant_u32(7, 0, None, None) == tk.TK_OK
+    assert L.tk_fill_constant_u32(7, 4, None, None) == tk.TK_EINVAL
+    assert L.tk_fill_constant_u32(7, 4, FAKE + 2, None) == tk.TK_EINVAL
+    assert L.tk_fill_constant_u32(7, 1 << 62, FAKE, None) == tk.TK_ERANGE
+
+
 def test_status_strings():
     for code in range(5):
         s = L.tk_status_string(code).decode()
@@ -172,9 +179,9 @@ def test_tunable_hook_validation():
     value restores the environment's setting (no device involved)."""
     ok = {"store_nt": (0, 1), "max_blocks": (1, 7, (1 << 31) - 1), "unroll": (1, 2, 4),
           "choice_tiles": (1, 2, 4, 8), "exp_tiles": (1, 2, 4), "zig_tiles": (1, 2, 4, 8, 16),
-          "zig_lds": (0, 1), "zig_fused": (0, 1)}
+          "zig_lds": (0, 1), "zig_fused": (0, 1), "const_work": (0, 1, 4096)}
     bad = {"store_nt": (2,), "max_blocks": (0, 1 << 31), "unroll": (3, 8), "choice_tiles": (3, 16),
-           "exp_tiles": (8,), "zig_tiles": (3, 32), "zig_lds": (2,), "zig_fused": (7,)}
+           "exp_tiles": (8,), "zig_tiles": (3, 32), "zig_lds": (2,), "zig_fused": (7,), "const_work": (4097,)}
     assert set(ok) == set(tk.TUNABLES)
     try:
         for name, values in ok.items():

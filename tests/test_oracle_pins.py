@@ -323,6 +323,16 @@ def test_bounded_fill_is_map_then_substream(s):
         assert out[k] == vv[0]
     if s == (1 << 31) + 1:
         assert 0.45 < (~acc).mean() < 0.55
+        # the retried values follow the uniform law on [0, s) by themselves (a retry that
+        # took a word correlated with the rejected one, or a fixed word, would not): 2^16
+        # draws at a start far from the others, about 2^15 of them retried, in 16 bins
+        big_start, m = 123456789, 1 << 16
+        o2 = oracle.fill_u32_below(key, big_start, m, s)
+        _, a2 = oracle.lemire32_map(oracle.fill_u32(key, big_start, m), s)
+        r = o2[~a2].astype(np.uint64)
+        assert r.size > 30000 and r.max() < s
+        assert stats.chisquare(np.bincount((r * 16 // s).astype(np.int64), minlength=16))[1] > 1e-4
+        assert stats.chisquare(np.bincount((o2.astype(np.uint64) * 16 // s).astype(np.int64), minlength=16))[1] > 1e-4
 
 
 def test_bounded64_fill_is_map_then_substream():

@@ -126,3 +126,12 @@ def test_zero_length_writes_nothing():
         b = DevBuf(0, np.dtype(dt).itemsize)
         fill(1, 0, 0, b.ptr)
         assert b.host(dt).size == 0
+
+
+def test_constant_fill():
+    """The store-ceiling kernel writes exactly its n words at any 4-byte alignment."""
+    for off in (0, 1, 3, 1021):
+        for n in (1, 5, 1023, 1024 + off, (1 << 20) + 3):
+            b = DevBuf(n, 4, 4 * off)
+            tk.tk_fill_constant_u32(0xDEADBEEF, n, b.ptr)
+            assert (b.host(np.uint32) == 0xDEADBEEF).all(), (off, n)

@@ -94,6 +94,13 @@ def check_normal_f64():
             assert counted in (None, int((path != 0).sum()))
 
 
+def check_constant():
+    for off in (0, 1, 3):
+        b = DevBuf(N, 4, 4 * off)
+        tk.tk_fill_constant_u32(0x01020304, N, b.ptr)
+        assert (b.host(np.uint32) == 0x01020304).all(), off
+
+
 def check_all():
     check_streaming()
     check_choice()
@@ -108,6 +115,7 @@ CASES = [
     ("exp_tiles", 1, check_exponential), ("exp_tiles", 4, check_exponential),
     ("zig_tiles", 1, check_normal_f64), ("zig_tiles", 2, check_normal_f64), ("zig_tiles", 8, check_normal_f64),
     ("zig_tiles", 16, check_normal_f64), ("zig_lds", 0, check_normal_f64), ("zig_fused", 0, check_normal_f64),
+    ("const_work", 16, check_constant), ("const_work", 200, check_constant),
 ]
 
 
