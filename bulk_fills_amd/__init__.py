@@ -82,6 +82,7 @@ SIGNATURES = {
     "tk_debug_fail_allocations": [_u32, _u32],
     "tk_debug_device_bytes": [_p],
     "tk_fill_constant_u32": [_u32, _u64, _p, _p],
+    "tk_fill_normal_f64_no_alloc": [_u32, _u64, _u64, _p, _p],
 }
 for _name, _args in SIGNATURES.items():
     _fn = getattr(lib, _name)
@@ -159,6 +160,7 @@ tk_fill_f64 = _fill("tk_fill_f64", 8)
 tk_fill_bool = _fill("tk_fill_bool", 1)
 tk_fill_normal_f64 = _fill("tk_fill_normal_f64", 8)
 tk_fill_normal_f32 = _fill("tk_fill_normal_f32", 4)
+tk_fill_normal_f64_no_alloc = _fill("tk_fill_normal_f64_no_alloc", 8)
 tk_fill_normal_f32_half_turn = _fill("tk_fill_normal_f32_half_turn", 4)
 tk_fill_randn_f32 = _fill("tk_fill_randn_f32", 4)
 tk_fill_exponential_f64 = _fill("tk_fill_exponential_f64", 8)

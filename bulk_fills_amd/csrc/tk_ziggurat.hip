@@ -694,11 +694,120 @@ static tk_status normal_f64_fill(ZigArgs a, uint64_t start_draw, uint64_t n, uin
   return TK_OK;
 }
 
+// ---------------------------------------------------------------------------------------
+// The f64 normal fill without allocation: the two-kernel path with its layer tables
+// compiled into device memory and its miss lists in one static device array
+// ---------------------------------------------------------------------------------------
+// Largest n per call, and the shape the scratch array is sized for: 256-lane table-pass
+// groups of 4 tiles (2048 elements each), whatever the launch tunables say.
+constexpr uint64_t kNoAllocMaxN = 1ull << 24;
+constexpr int kNoAllocTiles = 4;
+constexpr uint64_t kNoAllocGroups = (kNoAllocMaxN / 2 + kBlock * kNoAllocTiles - 1) / (kBlock * kNoAllocTiles);
+constexpr uint64_t kNoAllocSlot = zig_slot_entries(kBlock, kNoAllocTiles);  // entries per group
+constexpr uint64_t kNoAllocOvf = 65536;                                     // overflow entries
+// Layout in 32-bit words: the overflow counter (alone in the first 256 bytes), the per-group
+// miss counts, the per-group slots, the overflow list: 598080 words, 2.28 MiB per device.
+constexpr uint64_t kNoAllocCountsAt = 64;
+constexpr uint64_t kNoAllocSlotsAt = kNoAllocCountsAt + kNoAllocGroups;
+constexpr uint64_t kNoAllocOvfAt = kNoAllocSlotsAt + kNoAllocGroups * kNoAllocSlot;
+constexpr uint64_t kNoAllocWords = kNoAllocOvfAt + kNoAllocOvf;
+static_assert(kNoAllocCountsAt * 4 % 256 == 0 && kNoAllocSlotsAt % 64 == 0 && kNoAllocOvfAt % 64 == 0,
+              "each list starts on a 256-byte boundary");
+
+// Per-device copies (the code object is loaded on every device the library runs on, and
+// each holds its own arrays until the process ends).  Host code never uses these names as
+// addresses: it asks the runtime for each device's address once (hipGetSymbolAddress).
+static __device__ __align__(256) uint32_t scratch[kNoAllocWords];
+struct alignas(16) ZigPairRow {
+  double x, y;
+};
+static __device__ __align__(256) ZigPairRow zig_pairs_static[TK_ZIG_LAYERS] = {TK_ZIG_PAIR_ROWS};
+static __device__ __align__(256) double zig_f_static[TK_ZIG_LAYERS + 1] = {TK_ZIG_F_ROWS};
+
+struct NoAllocDevice {
+  std::mutex m;
+  bool ready = false;
+  uint32_t *scratch = nullptr;  // this device's `scratch`
+  const double2 *xx = nullptr;  // this device's `zig_pairs_static`
+  const double *f = nullptr;    // this device's `zig_f_static`
+};
+static NoAllocDevice g_no_alloc[kMaxDevices];
+
+// The device addresses of the static arrays on the current device, looked up on the
+// device's first call (with the device current) and kept.
+static tk_status no_alloc_init(NoAllocDevice &d) {
+  if (d.ready) return TK_OK;
+  void *p = nullptr, *px = nullptr, *pf = nullptr;
+  tk_status st;
+  if ((st = hip_status(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)))) != TK_OK) return st;
+  if ((st = hip_status(hipGetSymbolAddress(&px, HIP_SYMBOL(zig_pairs_static)))) != TK_OK) return st;
+  if ((st = hip_status(hipGetSymbolAddress(&pf, HIP_SYMBOL(zig_f_static)))) != TK_OK) return st;
+  if (!p || !px || !pf) return TK_EHIP;
+  d.scratch = (uint32_t *)p;
+  d.xx = (const double2 *)px;
+  d.f = (const double *)pf;
+  d.ready = true;
+  return TK_OK;
+}
+
+static tk_status normal_f64_no_alloc(uint32_t key, uint64_t start_draw, uint64_t n, double *out, hipStream_t stream) {
+  if (n == 0) return TK_OK;
+  if (!out || ((uintptr_t)out & 7u)) return TK_EINVAL;
+  if (n > kNoAllocMaxN) return TK_EINVAL;
+  if (start_draw > 0x7FFFFFFFull || n - 1 > 0x7FFFFFFFull - start_draw) return TK_ERANGE;
+  tk_status st;
+  const int dev = current_device(&st);
+  if (dev < 0) return st;
+  NoAllocDevice &d = g_no_alloc[dev];
+  {
+    std::lock_guard<std::mutex> lock(d.m);
+    if ((st = no_alloc_init(d)) != TK_OK) return st;
+  }
+  ZigArgs a{};
+  a.hk = host_lowbias32(key);
+  a.hkp = host_substream_key(key, kPurposeNormal64);
+  a.r = TK_ZIG_R;
+  a.out = out;
+  a.start = start_draw;
+  a.n = n;
+  a.head = ((uintptr_t)out & 15u) ? 1 : 0;
+  a.nvec = (n - a.head) / 2;
+  a.tail = (uint32_t)(n - a.head - 2 * a.nvec);
+  uint64_t groups = (a.nvec + kBlock * kNoAllocTiles - 1) / (kBlock * kNoAllocTiles);
+  if (groups == 0) groups = 1;
+  if (groups > kNoAllocGroups) return TK_EINVAL;  // not reached for n <= kNoAllocMaxN
+  a.ngroups = (uint32_t)groups;
+  a.slot_size = (uint32_t)kNoAllocSlot;
+  a.slot_cap = (uint32_t)kNoAllocSlot;
+  a.ovf_cap = (uint32_t)kNoAllocOvf;
+  a.xx = d.xx;
+  a.f = d.f;
+  a.ctr = d.scratch;
+  a.counts = d.scratch + kNoAllocCountsAt;
+  a.slots = d.scratch + kNoAllocSlotsAt;
+  a.ovf = d.scratch + kNoAllocOvfAt;
+  // the overflow count must start at zero (a kernel, not a memset: graph capture records
+  // no memset node); the per-group counts and slots are written by every table-pass group
+  hipLaunchKernelGGL(k_zig_reset, dim3(1), dim3(64), 0, stream, a.ctr);
+  if ((st = launch_status()) != TK_OK) return st;
+  launch_table_pass<kBlock, kNoAllocTiles, true, false, false>(a, stream);
+  if ((st = launch_status()) != TK_OK) return st;
+  const uint32_t gpb = (uint32_t)(kBlock * kBlock / (kBlock * kNoAllocTiles));
+  const uint64_t cgrid = (groups + gpb - 1) / gpb;
+  hipLaunchKernelGGL(k_zig_continue<false>, dim3((uint32_t)cgrid), dim3(kBlock), 0, stream, a, gpb);
+  return launch_status();
+}
+
 }  // namespace tk
 
 using namespace tk;
 
 extern "C" {
+
+tk_status tk_fill_normal_f64_no_alloc(uint32_t key, uint64_t start_draw, uint64_t n, double *out,
+                                      hipStream_t stream) {
+  return normal_f64_no_alloc(key, start_draw, n, out, stream);
+}
 
 tk_status tk_fill_normal_f64(uint32_t key, uint64_t start_draw, uint64_t n, double *out, hipStream_t stream) {
   ZigArgs a{};

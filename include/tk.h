@@ -114,6 +114,23 @@ tk_status tk_fill_i64_below(uint32_t key, uint64_t start_draw, uint64_t n, int64
 tk_status tk_fill_normal_f64(uint32_t key, uint64_t start_draw, uint64_t n, double *out, hipStream_t stream);
 tk_status tk_fill_normal_f32(uint32_t key, uint64_t start_draw, uint64_t n, float *out, hipStream_t stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, serving
+ * loops, harnesses that forbid hipMalloc): tk_fill_normal_f64 computed by its two-kernel
+ * path (table pass, then a continuation pass over the listed misses; the same values as
+ * tk_fill_normal_f64) with no allocation of any kind.  The layer tables are compiled into
+ * the library's device code, and the miss lists live in one static device array per device
+ * (2.28 MiB, held from the first call on that device until the process ends); the call
+ * enqueues three kernel launches on `stream` and nothing else.
+ *   n: at most 2^24 elements per call, else TK_EINVAL (cut a longer fill into pieces on
+ *      one stream: the pieces equal the whole fill).  Other arguments and errors as for
+ *      tk_fill_normal_f64 (out 8-byte aligned, i < 2^31).
+ *   Every call on a device uses that device's one array: calls that overlap in time on one
+ *   device (other streams, other threads) race and give wrong values.  Order them, e.g. on
+ *   one stream.  The array keeps the last call's contents; each call clears what must start
+ *   at zero itself.                                                                      */
+tk_status tk_fill_normal_f64_no_alloc(uint32_t key, uint64_t start_draw, uint64_t n, double *out,
+                                      hipStream_t stream);
+
 /* Normal variants (f32, i < 2^32 unless stated).
  * half_turn: tandem-sycl, "Design", §Normals shifts the Box-Muller angle by half a turn
  *   into [-pi, pi): the same pairs with angle 2 pi (u2 - 1/2), so both values are the

@@ -128,6 +128,15 @@ def test_philox_variant_validation():
     assert L.tk_philox_fill_choice_u32(1, 0, 4, None, FAKE, None) == tk.TK_EINVAL
 
 
+def test_no_alloc_normal_validation():
+    f = L.tk_fill_normal_f64_no_alloc
+    assert f(1, 0, 0, None, None) == tk.TK_OK
+    assert f(1, 0, 4, None, None) == tk.TK_EINVAL
+    assert f(1, 0, 4, FAKE + 4, None) == tk.TK_EINVAL       # not 8-byte aligned
+    assert f(1, 0, (1 << 24) + 1, FAKE, None) == tk.TK_EINVAL  # beyond the per-call limit
+    assert f(1, (1 << 31) - 1, 2, FAKE, None) == tk.TK_ERANGE
+
+
 def test_constant_fill_validation():
     assert L.tk_fill_constant_u32(7, 0, None, None) == tk.TK_OK
     assert L.tk_fill_constant_u32(7, 4, None, None) == tk.TK_EINVAL
