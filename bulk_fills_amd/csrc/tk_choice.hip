@@ -9,6 +9,8 @@
 #include <math.h>
 
 #include <deque>
+#include <memory>
+#include <new>
 #include <vector>
 
 #include "tk_device.h"
@@ -238,6 +240,40 @@ static tk_status choice_fill(ChoiceArgs a, uint64_t start_draw, uint64_t n, uint
   return launch_status();
 }
 
+// The body of tk_alias_create.  Every host allocation happens before the device one, so
+// an exception from them leaves nothing behind (the handle is owned until returned).
+static tk_status alias_create(const double *weights, uint32_t n, tk_alias **table) {
+  std::unique_ptr<tk_alias> t(new tk_alias());
+  t->n = n;
+  t->table = nullptr;
+  if (!build_alias(weights, n, t->q, t->alias)) return TK_EINVAL;  // weights are checked before any HIP call
+  tk_status st;
+  const int dev = current_device(&st);
+  if (dev < 0) return st;
+  t->device = dev;
+  // padded to an even number of columns: the fill copies the table 16 bytes at a time
+  const uint32_t padded = (n + 1) & ~1u;
+  std::vector<uint2> packed(padded, make_uint2(0u, 0u));
+  for (uint32_t j = 0; j < n; ++j) packed[j] = make_uint2(t->q[j], t->alias[j]);
+  if (device_alloc((void **)&t->table, padded * sizeof(uint2)) != hipSuccess) return TK_ENOMEM;
+  if ((st = hip_status(hipMemcpy(t->table, packed.data(), padded * sizeof(uint2), hipMemcpyHostToDevice))) != TK_OK) {
+    (void)device_free(t->table, padded * sizeof(uint2));
+    return st;
+  }
+  *table = t.release();
+  return TK_OK;
+}
+
+static tk_status alias_build_host(const double *weights, uint32_t n, uint32_t *q, uint32_t *alias) {
+  std::vector<uint32_t> vq, va;
+  if (!build_alias(weights, n, vq, va)) return TK_EINVAL;
+  for (uint32_t j = 0; j < n; ++j) {
+    q[j] = vq[j];
+    alias[j] = va[j];
+  }
+  return TK_OK;
+}
+
 }  // namespace tk
 
 using namespace tk;
@@ -247,35 +283,13 @@ extern "C" {
 tk_status tk_alias_create(const double *weights, uint32_t n, tk_alias **table) {
   if (!weights || !table || n == 0 || n > (1u << 24)) return TK_EINVAL;
   *table = nullptr;
-  tk_alias *t = new tk_alias();
-  t->n = n;
-  t->table = nullptr;
-  if (!build_alias(weights, n, t->q, t->alias)) {  // weights are checked before any HIP call
-    delete t;
-    return TK_EINVAL;
-  }
-  tk_status st;
-  const int dev = current_device(&st);
-  if (dev < 0) {
-    delete t;
-    return st;
-  }
-  t->device = dev;
-  // padded to an even number of columns: the fill copies the table 16 bytes at a time
-  const uint32_t padded = (n + 1) & ~1u;
-  std::vector<uint2> packed(padded, make_uint2(0u, 0u));
-  for (uint32_t j = 0; j < n; ++j) packed[j] = make_uint2(t->q[j], t->alias[j]);
-  if (device_alloc((void **)&t->table, padded * sizeof(uint2)) != hipSuccess) {
-    delete t;
+  // the host-side construction allocates (up to a few hundred MB for 2^24 columns); a
+  // failed host allocation returns TK_ENOMEM instead of leaving the C ABI as an exception
+  try {
+    return alias_create(weights, n, table);
+  } catch (const std::bad_alloc &) {
     return TK_ENOMEM;
   }
-  if ((st = hip_status(hipMemcpy(t->table, packed.data(), padded * sizeof(uint2), hipMemcpyHostToDevice))) != TK_OK) {
-    (void)device_free(t->table, padded * sizeof(uint2));
-    delete t;
-    return st;
-  }
-  *table = t;
-  return TK_OK;
 }
 
 tk_status tk_alias_destroy(tk_alias *t) {
@@ -290,13 +304,11 @@ uint32_t tk_alias_size(const tk_alias *t) { return t ? t->n : 0; }
 
 tk_status tk_alias_build_host(const double *weights, uint32_t n, uint32_t *q, uint32_t *alias) {
   if (!weights || !q || !alias || n == 0 || n > (1u << 24)) return TK_EINVAL;
-  std::vector<uint32_t> vq, va;
-  if (!build_alias(weights, n, vq, va)) return TK_EINVAL;
-  for (uint32_t j = 0; j < n; ++j) {
-    q[j] = vq[j];
-    alias[j] = va[j];
+  try {
+    return alias_build_host(weights, n, q, alias);
+  } catch (const std::bad_alloc &) {
+    return TK_ENOMEM;
   }
-  return TK_OK;
 }
 
 tk_status tk_alias_export(const tk_alias *t, uint32_t *q, uint32_t *alias) {

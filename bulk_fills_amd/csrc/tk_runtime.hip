@@ -1,4 +1,5 @@
 // tk_runtime.hip -- status strings, per-thread error state, tunables, device queries.
+#include <stdio.h>
 #include <stdlib.h>
 #include <string.h>
 
@@ -93,7 +94,12 @@ static void apply_env_failures() {
   std::call_once(once, [] {
     const uint64_t n = env_u64("TK_DEBUG_FAIL_ALLOC", 0);
     std::lock_guard<std::mutex> lock(g_alloc_mutex);
-    if (n) g_alloc_fail = n > 0xFFFFFFFFull ? 0xFFFFFFFFu : (uint32_t)n;
+    if (n) {
+      g_alloc_fail = n > 0xFFFFFFFFull ? 0xFFFFFFFFu : (uint32_t)n;
+      // said once, so that a forced TK_ENOMEM is never taken for a real one
+      fprintf(stderr, "libtk: TK_DEBUG_FAIL_ALLOC=%llu is set: the first %u device allocations of this "
+              "process fail with TK_ENOMEM (a test hook)\n", (unsigned long long)n, g_alloc_fail);
+    }
   });
 }
 

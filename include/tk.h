@@ -261,7 +261,8 @@ tk_status tk_debug_last_miss_count(uint64_t *count);
  * tables it created; a failed growth releases all the miss lists); a later call allocates
  * again.  count = 0 cancels.  Process-wide, for every device and thread.  A real
  * allocation failure takes the same path.  The environment variable TK_DEBUG_FAIL_ALLOC=<n>
- * makes the process's first n allocations fail the same way (a call here replaces it). */
+ * makes the process's first n allocations fail the same way (a call here replaces it), and
+ * the library says so once on stderr. */
 tk_status tk_debug_fail_allocations(uint32_t skip, uint32_t count);
 /* Test hook: the device memory the library holds now, in bytes, over all devices: the
  * per-device ziggurat state (held until the process ends) and the live alias tables. */

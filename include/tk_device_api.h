@@ -15,11 +15,10 @@
  * bit for bit, where hk = tk_key_hash(key) (computed once, on the host or the device).
  * Counters are 32-bit: a kernel that needs more than 2^32 words per key takes a new key.
  *
- * Counter discipline (Phobos, §Random numbers): use each element's flat index in the
- * whole tensor as its counter, not its index in the block, so that no two elements of a
- * launch share a draw.  tk_randn*_f32 reads words 2c and 2c+1, so a kernel that takes
- * both uniforms and normals from one key must give them disjoint counter ranges (or
- * separate keys).
+ * Counters (Phobos, §Random numbers): a counter must be unique across the whole launch,
+ * which a block-local index is not; the element's global flat index is.  tk_randn*_f32
+ * consumes two words per counter (2c and 2c+1), so mixed uses of one key need disjoint
+ * counter ranges, or different keys.
  *
  * Each float transform is a fixed sequence of IEEE operations and gfx950 hardware
  * instructions with nothing a compiler may contract, so the values do not depend on the

@@ -137,6 +137,37 @@ def test_no_alloc_normal_validation():
     assert f(1, (1 << 31) - 1, 2, FAKE, None) == tk.TK_ERANGE
 
 
+_ALIAS_OOM_CHILD = """
+import ctypes as C, resource, sys
+import numpy as np
+lib = C.CDLL(sys.argv[1])
+n = 1 << 24
+w = np.ones(n)
+q = np.empty(n, dtype=np.uint32)
+a = np.empty(n, dtype=np.uint32)
+lib.tk_alias_build_host.argtypes = [C.c_void_p, C.c_uint32, C.c_void_p, C.c_void_p]
+lib.tk_alias_create.argtypes = [C.c_void_p, C.c_uint32, C.c_void_p]
+ok = lib.tk_alias_build_host(w.ctypes.data, n, q.ctypes.data, a.ctypes.data)
+used = int(open("/proc/self/statm").read().split()[0]) * resource.getpagesize()
+resource.setrlimit(resource.RLIMIT_AS, (used + (64 << 20), resource.RLIM_INFINITY))
+bad = lib.tk_alias_build_host(w.ctypes.data, n, q.ctypes.data, a.ctypes.data)
+h = C.c_void_p()
+bad2 = lib.tk_alias_create(w.ctypes.data, n, C.byref(h))
+print(ok, bad, bad2, h.value is None)
+"""
+
+
+def test_alias_host_allocation_failure_is_enomem():
+    """A host allocation failure while building a 2^24-column table (forced in a child
+    process by an address-space limit) returns TK_ENOMEM through the C ABI and creates no
+    handle, instead of ending the caller with an exception."""
+    import subprocess
+    import sys
+    out = subprocess.run([sys.executable, "-c", _ALIAS_OOM_CHILD, tk.LIB_PATH], check=True,
+                         capture_output=True, text=True, timeout=120).stdout.split()
+    assert out == [str(tk.TK_OK), str(tk.TK_ENOMEM), str(tk.TK_ENOMEM), "True"], out
+
+
 def test_constant_fill_validation():
     assert L.tk_fill_constant_u32(7, 0, None, None) == tk.TK_OK
     assert L.tk_fill_constant_u32(7, 4, None, None) == tk.TK_EINVAL

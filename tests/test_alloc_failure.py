@@ -42,6 +42,23 @@ def test_failures_from_the_environment():
     print(r.stdout[-4000:], r.stderr[-4000:], flush=True)
     assert r.returncode == 0, f"exit status {r.returncode}"
     assert "alloc_failure_child: ok" in r.stdout
+    assert r.stderr.count("TK_DEBUG_FAIL_ALLOC=2 is set") == 1  # announced once
+
+
+def test_environment_hook_announces_itself():
+    """TK_DEBUG_FAIL_ALLOC is read once and reported on stderr (no device needed: the hook
+    call reads the environment before anything else)."""
+    code = ("import ctypes, sys; lib = ctypes.CDLL(sys.argv[1]); "
+            "lib.tk_debug_fail_allocations(0, 0); lib.tk_debug_fail_allocations(0, 0)")
+    env = dict(os.environ, TK_DEBUG_FAIL_ALLOC="3")
+    r = subprocess.run([sys.executable, "-c", code, tk.LIB_PATH], env=env, capture_output=True, text=True,
+                       timeout=60)
+    assert r.returncode == 0, r.stderr
+    assert r.stderr.count("libtk: TK_DEBUG_FAIL_ALLOC=3 is set") == 1, r.stderr
+    env.pop("TK_DEBUG_FAIL_ALLOC")
+    r = subprocess.run([sys.executable, "-c", code, tk.LIB_PATH], env=env, capture_output=True, text=True,
+                       timeout=60)
+    assert "TK_DEBUG_FAIL_ALLOC" not in r.stderr
 
 
 @pytest.mark.gpu
