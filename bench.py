@@ -31,7 +31,7 @@ HBM_PEAK_GBS = 8000.0
 # dependent integer steps per lane before each store of the constant fill, swept for the
 # store ceiling (stores spaced by some arithmetic, as in the fills, can go faster than
 # stores issued back to back)
-CONST_WORK = (0, 8, 16, 32, 64, 128)
+CONST_WORK = (0, 8, 12, 16, 20, 24, 32, 64)
 
 
 def parse():
@@ -160,7 +160,30 @@ def build_step(tk, torch, n):
         for work in CONST_WORK:
             ceil_rows.append((f"constant_fill_work{work}", nb, const_fill(nb, work)))
         ceil_rows.append(("hipMemsetAsync", nb, (lambda nb: lambda s: memset(nb))(nb)))
-    return fills, next_rows, calib, start_rows, ceil_rows, (out, x, table)
+    # the store pattern, 2 GiB: consecutive 4 KiB tiles per work-group (one, two or four),
+    # a capped grid whose groups stride over the output, for the constant fill, the f64
+    # fill and the ziggurat (whose table pass runs four tiles per group)
+    def tuned(fn, **tunables):
+        def f(s):
+            for k, v in tunables.items():
+                tk.tk_debug_set_tunable(k, v)
+            try:
+                fn(s)
+            finally:
+                for k in tunables:
+                    tk.tk_debug_set_tunable(k, -1)
+        return f
+    c2 = lambda s: tk.tk_fill_constant_u32(0, 2 * n, optr)
+    f64 = lambda s: tk.tk_fill_f64(1, 0, n, optr)
+    zig = lambda s: tk.tk_fill_normal_f64(1, 0, n, optr)
+    pattern_rows = [("constant_fill", 8 * n, c2), ("constant_fill tiles=2", 8 * n, tuned(c2, unroll=2)),
+                    ("constant_fill tiles=4", 8 * n, tuned(c2, unroll=4)),
+                    ("constant_fill grid=8192", 8 * n, tuned(c2, max_blocks=8192)),
+                    ("f64", 8 * n, f64), ("f64 tiles=4", 8 * n, tuned(f64, unroll=4)),
+                    ("normal_f64 tiles=2", 8 * n, tuned(zig, zig_tiles=2)),
+                    ("normal_f64 tiles=4", 8 * n, tuned(zig, zig_tiles=4)),
+                    ("normal_f64 tiles=8", 8 * n, tuned(zig, zig_tiles=8))]
+    return fills, next_rows, calib, start_rows, ceil_rows, pattern_rows, (out, x, table)
 
 
 class FenceFreeEvent:
@@ -373,11 +396,11 @@ def main():
     import tk_inputs as ti
 
     n = ti.FULL_N
-    fills, next_rows, calib, start_rows, ceil_rows, keep = build_step(tk, torch, n)
+    fills, next_rows, calib, start_rows, ceil_rows, pattern_rows, keep = build_step(tk, torch, n)
     if args.only:
         wanted = set(args.only.split(","))
         fills = [f for f in fills + next_rows + [calib] if f[0] in wanted]
-        next_rows, start_rows, ceil_rows = [], [], []
+        next_rows, start_rows, ceil_rows, pattern_rows = [], [], [], []
     torch.cuda.synchronize()
 
     def step(s, events=None):
@@ -482,6 +505,13 @@ def main():
         per_start.setdefault(fill, {})[str(s0)] = r = row_record(nb, 0, rt.time(fn, warm / 4))
         progress(f"{fill} start {s0}: {r['median_us']} us")
 
+    store_pattern = {}
+    for name, nb, fn in pattern_rows:
+        r = rt.time(fn, warm / 4)
+        store_pattern[name] = {"GiB_per_s": round(rate(nb, r["median_ms"]), 1),
+                               "median_us": round(r["median_ms"] * 1e3, 2), "min_us": round(r["min_ms"] * 1e3, 2)}
+        progress(f"store pattern {name}: {store_pattern[name]['median_us']} us")
+
     progress("CPU oracle baseline")
     cpu = None if args.no_cpu else cpu_baseline(n, args.cpu_single_log2)
 
@@ -505,6 +535,7 @@ def main():
         "store_ceiling": {"best": ceiling_best, "rows": ceiling},
         "fills": per_fill,
         "per_start": per_start,
+        "store_pattern": store_pattern,
         "next_rows": nxt,
         "device": device_info(),
     }

@@ -220,13 +220,17 @@ struct OpWord64 : FillBase<uint64_t> {
 };
 
 // Four consecutive stream words starting `shift` bytes into word w0: lane-local words
-// w0..w0+3, the fifth from the next lane (the last lane of the wave hashes it).
-// `shift` is uniform across the launch.
+// w0..w0+3, the fifth from the next lane.  The last lane's fifth word is the next wave's
+// first, w0 of lane 0 plus 256: its counter is the same for the whole wave, so it is hashed
+// once per wave on the scalar unit (about eight scalar instructions) instead of by every
+// lane.  All 64 lanes must be active (lane 0's w0 is read with readfirstlane).  `shift` is
+// uniform across the launch.
 __device__ __forceinline__ uint4 words_at_byte(uint32_t hk, uint32_t w0, uint32_t shift) {
   uint32_t a0 = word(hk, w0), a1 = word(hk, w0 + 1), a2 = word(hk, w0 + 2), a3 = word(hk, w0 + 3);
   if (shift == 0) return u4(a0, a1, a2, a3);
+  const uint32_t next_wave = word(hk, (uint32_t)__builtin_amdgcn_readfirstlane(w0) + 256u);
   uint32_t a4 = from_next_lane(a0);
-  if (lane_id() == 63) a4 = word(hk, w0 + 4);
+  if (lane_id() == 63) a4 = next_wave;
   return u4(__builtin_amdgcn_alignbyte(a1, a0, shift), __builtin_amdgcn_alignbyte(a2, a1, shift),
             __builtin_amdgcn_alignbyte(a3, a2, shift), __builtin_amdgcn_alignbyte(a4, a3, shift));
 }
@@ -366,11 +370,16 @@ struct OpNormalF32 : FillBase<float> {
     pair(c0 + 1, &c, &d);
     if ((i0 & 1u) == 0) return u4(__float_as_uint(a), __float_as_uint(b), __float_as_uint(c), __float_as_uint(d));
     // Odd start: the vector is sin(c0), pair c0+1, cos(c0+2); cos(c0+2) is the next
-    // lane's first value.
+    // lane's first value.  The last lane's is the next wave's first pair, lane 0's c0 plus
+    // 128, the same for the whole wave: its two words are hashed on the scalar unit and
+    // only the cosine's arithmetic runs on the vector unit, once for the wave (all 64
+    // lanes must be active: lane 0's c0 is read with readfirstlane).
     float e = from_next_lane(a);
-    if (!overlap && lane_id() == 63) {
-      float s_unused;
-      pair(c0 + 2, &e, &s_unused);
+    if (!overlap) {
+      const uint32_t cn = (uint32_t)__builtin_amdgcn_readfirstlane(c0) + 128u;
+      float en, s_unused;
+      pair(cn, &en, &s_unused);
+      if (lane_id() == 63) e = en;
     }
     return u4(__float_as_uint(b), __float_as_uint(c), __float_as_uint(d), __float_as_uint(e));
   }
@@ -430,14 +439,27 @@ struct OpExpF32 : FillBase<uint32_t> {
 };
 
 // Exponential fills: T 4 KiB tiles per work-group after copying the fill's 4 KiB logarithm
-// table to LDS (one 16-byte load per thread), so the per-element table reads are ds_reads
-// and not L1 gathers through the texture addresser.
+// table to LDS (16-byte loads, all issued before the LDS writes),
+// so the per-element table reads are ds_reads and not L1 gathers through the texture
+// addresser.
 template <class Op, int T, bool kNT>
 __global__ __launch_bounds__(kBlock) void k_exp_fill(Op op) {
   using Entry = typename Op::Entry;
-  static_assert(sizeof(Entry) * Op::kEntries == 16 * kBlock, "one 16-byte piece of the table per thread");
-  __shared__ Entry tab[Op::kEntries];
-  ((uint4 *)tab)[threadIdx.x] = ((const uint4 *)Op::table())[threadIdx.x];
+  constexpr int kPieces = (int)(sizeof(Entry) * Op::kEntries / 16);
+  constexpr int kPer = (kPieces + kBlock - 1) / kBlock;
+  static_assert(sizeof(Entry) * Op::kEntries % 16 == 0, "the table copies in 16-byte pieces");
+  __shared__ __align__(16) Entry tab[Op::kEntries];
+  uint4 piece[kPer];
+#pragma unroll
+  for (int r = 0; r < kPer; ++r) {
+    const int i = (int)threadIdx.x + r * kBlock;
+    if (i < kPieces) piece[r] = ((const uint4 *)Op::table())[i];
+  }
+#pragma unroll
+  for (int r = 0; r < kPer; ++r) {
+    const int i = (int)threadIdx.x + r * kBlock;
+    if (i < kPieces) ((uint4 *)tab)[i] = piece[r];
+  }
   __syncthreads();
   const uint64_t v0 = (uint64_t)blockIdx.x * T * kBlock + threadIdx.x;
 #pragma unroll
