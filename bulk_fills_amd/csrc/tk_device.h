@@ -172,6 +172,27 @@ __device__ __forceinline__ U32x4 philox4x32_10_ctr(uint32_t c0, uint32_t c1, uin
   return {c0, c1, c2, c3};
 }
 
+// The same rounds written with plain xors, for a block whose counter and key are the same
+// across the wave: the compiler keeps it on the scalar unit (s_mul_hi_u32, s_mul_i32,
+// s_xor_b32), where v_bitop3 would move it to the vector unit.
+__device__ __forceinline__ U32x4 philox4x32_10_uniform(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t k0,
+                                                       uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    c1 = (uint32_t)p1;
+    c3 = (uint32_t)p0;
+    c0 = n0;
+    c2 = n2;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return {c0, c1, c2, c3};
+}
+
 // Primary block b: counter (lo32 b, hi32 b, 0, 0).
 __device__ __forceinline__ U32x4 philox4x32_10(uint64_t block, uint32_t k0, uint32_t k1) {
   return philox4x32_10_ctr((uint32_t)block, (uint32_t)(block >> 32), 0u, 0u, k0, k1);

@@ -131,6 +131,46 @@ static tk_status launch_vec_overlap(Op op, hipStream_t stream) {
   return launch_status();
 }
 
+// Philox fills at word offsets o = 1..3 staged through LDS (the tile kernel).  Each
+// work-group writes one 4 KiB tile, as the aligned fills do: every lane computes its own
+// block-aligned Philox block, the one the first word of its vector falls in, and writes it
+// to LDS; the block after the tile, whose counter is the same for the whole group, is
+// computed once on the scalar unit by the last wave.  After one barrier each lane reads
+// its four words at word offset o from LDS and stores one 16-byte vector.  The shape of the
+// stores is that of the aligned fills (whole 4 KiB tiles per group, 1 KiB per wave).
+template <class Op, bool kNT>
+__global__ __launch_bounds__(kBlock) void k_philox_tile(Op op) {
+  __shared__ uint4 blk[kBlock + 1];
+  const uint64_t v0 = (uint64_t)blockIdx.x * kBlock;
+  const uint64_t wt = op.word0(v0);  // first word of the tile: 4 (b0 + lane) + o for each lane
+  const uint64_t b0 = wt >> 2;
+  const U32x4 B = philox4x32_10(b0 + threadIdx.x, op.k0, op.k1);
+  blk[threadIdx.x] = make_uint4(B.a, B.b, B.c, B.d);
+  if ((uint32_t)__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) == kBlock / 64 - 1) {
+    const uint64_t bn = b0 + kBlock;  // uniform counter: scalar unit
+    const U32x4 N = philox4x32_10_uniform((uint32_t)bn, (uint32_t)(bn >> 32), 0u, 0u, op.k0, op.k1);
+    if (lane_id() == 0) blk[kBlock] = make_uint4(N.a, N.b, N.c, N.d);
+  }
+  __syncthreads();
+  const uint32_t *wp = (const uint32_t *)blk + 4 * threadIdx.x + (uint32_t)(wt & 3u);
+  const uint64_t v = v0 + threadIdx.x;
+  const uint4 r = op.from_words(v, make_uint4(wp[0], wp[1], wp[2], wp[3]));
+  if (v < op.nvec) store16<kNT>(op.vec_ptr(v), r);
+  if (blockIdx.x == 0) write_edges(op);
+}
+
+template <class Op>
+static tk_status launch_philox_tile(const Op &op, hipStream_t stream) {
+  uint64_t grid = (op.nvec + kBlock - 1) / kBlock;
+  if (grid == 0) grid = 1;
+  if (grid > 0x7FFFFFFFull) return TK_EINVAL;
+  if (config().nt_stores)
+    hipLaunchKernelGGL((k_philox_tile<Op, true>), dim3((uint32_t)grid), dim3(kBlock), 0, stream, op);
+  else
+    hipLaunchKernelGGL((k_philox_tile<Op, false>), dim3((uint32_t)grid), dim3(kBlock), 0, stream, op);
+  return launch_status();
+}
+
 // One vector per lane and one 4 KiB tile per work-group over a grid as large as the
 // output measured fastest for streaming stores on MI355X (more vectors per lane or a
 // persistent grid lowered the store rate); TK_UNROLL=2|4 selects the alternatives.
@@ -542,15 +582,18 @@ struct OpDropout : FillBase<float> {
 // ---------------------------------------------------------------------------------------
 // Philox4x32-10 word source
 // ---------------------------------------------------------------------------------------
+// Every Philox streaming op builds vector v from the four consecutive words at word0(v)
+// (four words per vector: 32-bit draws one word each, 64-bit draws two) with
+// from_words(v, w); vec(v) computes those words in registers, the tile kernel stages them
+// through LDS.
 template <bool kFloat>
 struct OpPhilox32 : FillBase<uint32_t> {
   uint32_t k0, k1;
   __device__ __forceinline__ uint32_t xf(uint32_t w) const { return kFloat ? __float_as_uint(unit23(w)) : w; }
   __device__ __forceinline__ uint32_t elem(uint64_t k) const { return xf(philox_word(start + k, k0, k1)); }
-  __device__ __forceinline__ uint4 vec(uint64_t v) const {
-    uint4 w = philox_words(vec_draw(v), k0, k1, overlap);
-    return u4(xf(w.x), xf(w.y), xf(w.z), xf(w.w));
-  }
+  __device__ __forceinline__ uint64_t word0(uint64_t v) const { return vec_draw(v); }
+  __device__ __forceinline__ uint4 from_words(uint64_t, uint4 w) const { return u4(xf(w.x), xf(w.y), xf(w.z), xf(w.w)); }
+  __device__ __forceinline__ uint4 vec(uint64_t v) const { return from_words(v, philox_words(word0(v), k0, k1, overlap)); }
 };
 
 template <bool kFloat>
@@ -564,11 +607,12 @@ struct OpPhilox64 : FillBase<uint64_t> {
     const uint64_t w = 2 * (start + k);
     return xf(philox_word(w, k0, k1), philox_word(w + 1, k0, k1));
   }
-  __device__ __forceinline__ uint4 vec(uint64_t v) const {
-    uint4 w = philox_words(2 * vec_draw(v), k0, k1, overlap);
-    uint64_t a = xf(w.x, w.y), b = xf(w.z, w.w);
+  __device__ __forceinline__ uint64_t word0(uint64_t v) const { return 2 * vec_draw(v); }
+  __device__ __forceinline__ uint4 from_words(uint64_t, uint4 w) const {
+    const uint64_t a = xf(w.x, w.y), b = xf(w.z, w.w);
     return u4(lo32(a), hi32(a), lo32(b), hi32(b));
   }
+  __device__ __forceinline__ uint4 vec(uint64_t v) const { return from_words(v, philox_words(word0(v), k0, k1, overlap)); }
 };
 
 // ---------------------------------------------------------------------------------------
@@ -581,11 +625,12 @@ struct OpPhiloxBelow32 : FillBase<uint32_t> {
     return lemire32_sub(w, s, t, PhiloxSub(k0, k1, i, kPurposeBelow32));
   }
   __device__ __forceinline__ uint32_t elem(uint64_t k) const { return one(philox_word(start + k, k0, k1), start + k); }
-  __device__ __forceinline__ uint4 vec(uint64_t v) const {
+  __device__ __forceinline__ uint64_t word0(uint64_t v) const { return vec_draw(v); }
+  __device__ __forceinline__ uint4 from_words(uint64_t v, uint4 w) const {
     const uint64_t i = vec_draw(v);
-    const uint4 w = philox_words(i, k0, k1, overlap);
     return u4(one(w.x, i), one(w.y, i + 1), one(w.z, i + 2), one(w.w, i + 3));
   }
+  __device__ __forceinline__ uint4 vec(uint64_t v) const { return from_words(v, philox_words(word0(v), k0, k1, overlap)); }
 };
 
 template <bool kSmall>
@@ -599,12 +644,13 @@ struct OpPhiloxBelow64 : FillBase<uint64_t> {
     const uint64_t i = start + k;
     return one(philox_word(2 * i, k0, k1), philox_word(2 * i + 1, k0, k1), i);
   }
-  __device__ __forceinline__ uint4 vec(uint64_t v) const {
+  __device__ __forceinline__ uint64_t word0(uint64_t v) const { return 2 * vec_draw(v); }
+  __device__ __forceinline__ uint4 from_words(uint64_t v, uint4 w) const {
     const uint64_t i = vec_draw(v);
-    const uint4 w = philox_words(2 * i, k0, k1, overlap);
     const uint64_t a = one(w.x, w.y, i), b = one(w.z, w.w, i + 1);
     return u4(lo32(a), hi32(a), lo32(b), hi32(b));
   }
+  __device__ __forceinline__ uint4 vec(uint64_t v) const { return from_words(v, philox_words(word0(v), k0, k1, overlap)); }
 };
 
 // Box-Muller pairs over Philox words (pair c: words 2c and 2c+1), laid out as OpNormalF32.
@@ -675,10 +721,19 @@ tk_status run_simple(Op op, T *out, uint64_t start, uint64_t n, hipStream_t stre
   return launch_vec(op, stream);
 }
 
-// Philox fills whose vectors straddle blocks when (start + head) & mask != 0: the
-// overlapping-wave kernel then, the plain one otherwise.
+// Philox fills whose vectors straddle blocks when (start + head) & mask != 0: the tile
+// kernel or the overlapping-wave kernel then (tunable "philox_lds"), the plain one
+// otherwise.
 template <class Op, class T>
 tk_status run_straddling(Op op, T *out, uint64_t start, uint64_t n, uint32_t mask, hipStream_t stream) {
+  set_geometry(op, out, start, n);
+  if (((op.start + op.head) & mask) == 0) return launch_vec(op, stream);
+  return config().philox_lds ? launch_philox_tile(op, stream) : launch_vec_overlap(op, stream);
+}
+
+// The same for ops without a tile form (the Philox Box-Muller pairs).
+template <class Op, class T>
+tk_status run_straddling_overlap(Op op, T *out, uint64_t start, uint64_t n, uint32_t mask, hipStream_t stream) {
   set_geometry(op, out, start, n);
   return ((op.start + op.head) & mask) ? launch_vec_overlap(op, stream) : launch_vec(op, stream);
 }
@@ -937,7 +992,7 @@ tk_status tk_philox_fill_normal_f32(uint64_t key, uint64_t start_draw, uint64_t 
   TK_PRECHECK(out, ~0ull);
   OpPhiloxNormalF32 op{};
   op.k0 = (uint32_t)key; op.k1 = (uint32_t)(key >> 32);
-  return run_straddling(op, out, start_draw, n, 3u, stream);
+  return run_straddling_overlap(op, out, start_draw, n, 3u, stream);
 }
 
 tk_status tk_philox_fill_f64(uint64_t key, uint64_t start_draw, uint64_t n, double *out, hipStream_t stream) {

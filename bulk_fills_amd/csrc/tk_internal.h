@@ -52,6 +52,8 @@ struct Config {
   std::atomic<int> zig_tiles;        // TK_ZIG_TILES: tiles (one 16-byte vector per lane) per table-pass work-group
   std::atomic<bool> zig_fused;       // TK_ZIG_MODE=fused|split: misses finished in the table pass, or in a second kernel
   std::atomic<bool> zig_lds;         // TK_ZIG_TABLE=lds|global: where the table pass gathers the layers
+  std::atomic<bool> philox_lds;      // TK_PHILOX=lds|overlap: Philox fills at word offsets 1..3 by the LDS
+                                     // tile kernel or the overlapping-wave kernel
   std::atomic<int> const_work;       // TK_CONST_WORK: dependent integer steps per lane before each store of
                                      // the constant fill (0: none), to sweep the store ceiling's spacing
 };

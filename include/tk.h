@@ -280,6 +280,8 @@ tk_status tk_debug_device_bytes(uint64_t *bytes);
  *   "zig_lds" 0|1         ziggurat layer gathers from an LDS copy or from L1/L2 (TK_ZIG_TABLE)
  *   "zig_fused" 0|1       ziggurat misses finished in the table pass or a second kernel
  *                         (TK_ZIG_MODE; tk_debug_set_normal_f64_mode overrides it)
+ *   "philox_lds" 0|1      Philox fills at word offsets 1..3 by the LDS tile kernel (1) or
+ *                         the overlapping-wave kernel (0) (TK_PHILOX=lds|overlap)
  *   "const_work" 0..4096  dependent integer steps per lane before each store of
  *                         tk_fill_constant_u32 (TK_CONST_WORK; 0 = none): the spacing of
  *                         the store-ceiling measurement

@@ -101,6 +101,19 @@ def check_constant():
         assert (b.host(np.uint32) == 0x01020304).all(), off
 
 
+def check_philox():
+    for s in (0, 1, 2, 3, 5):
+        for fill, orc, isz, dt in ((tk.tk_philox_fill_u32, oracle.philox_fill_u32, 4, np.uint32),
+                                   (tk.tk_philox_fill_f32, oracle.philox_fill_f32, 4, np.float32),
+                                   (tk.tk_philox_fill_u64, oracle.philox_fill_u64, 8, np.uint64),
+                                   (tk.tk_philox_fill_f64, oracle.philox_fill_f64, 8, np.float64)):
+            assert_bits_equal(run(fill, PK, s, isz, dt), orc(PK, s, N), f"{fill.__name__} s={s}")
+        assert_bits_equal(run(tk.tk_philox_fill_u32_below, PK, s, 4, np.uint32, 1000),
+                          oracle.philox_fill_u32_below(PK, s, N, 1000), f"philox u32_below s={s}")
+        assert_bits_equal(run(tk.tk_philox_fill_u64_below, PK, s, 8, np.uint64, (1 << 63) + 1),
+                          oracle.philox_fill_u64_below(PK, s, N, (1 << 63) + 1), f"philox u64_below s={s}")
+
+
 def check_all():
     check_streaming()
     check_choice()
@@ -116,6 +129,7 @@ CASES = [
     ("zig_tiles", 1, check_normal_f64), ("zig_tiles", 2, check_normal_f64), ("zig_tiles", 8, check_normal_f64),
     ("zig_tiles", 16, check_normal_f64), ("zig_lds", 0, check_normal_f64), ("zig_fused", 0, check_normal_f64),
     ("const_work", 16, check_constant), ("const_work", 200, check_constant),
+    ("philox_lds", 0, check_philox), ("philox_lds", 1, check_philox),
 ]
 
 
