@@ -32,6 +32,154 @@ HBM_PEAK_GBS = 8000.0
 # store ceiling (stores spaced by some arithmetic, as in the fills, can go faster than
 # stores issued back to back)
 CONST_WORK = (0, 8, 12, 16, 20, 24, 32, 64)
+# a constant fill of MARKER_N words (one work-group, a grid no other launch has) right before
+# and right after the timed steps, so that a kernel trace can pick out the timed region
+TIMED_MARKER, MARKER_N = 0x7E57AB1E, 64
+
+
+# ---- summaries of rocprofv3 output (run on the GPU host after a profiled bench) --------
+# The kernel behind each fill's 2^28-element launch, by a prefix of its name in the
+# profiler's records (the fill's launch is its kernel's largest grid).
+FILL_KERNELS = {
+    "normal_f64": "void tk::k_zig_table_pass<256, 4, true, false, true, false>",
+    "dropout_f32": "void tk::k_vec_fill<tk::OpDropout, 1, true>",
+    "u64": "void tk::k_vec_fill<tk::OpWord64<false>, 1, false>",
+    "f64": "void tk::k_vec_fill<tk::OpWord64<true>, 1, false>",
+    "u32": "void tk::k_vec_fill<tk::OpWord32<false>, 1, false>",
+    "f16_bits": "void tk::k_vec_fill<tk::OpSub16<true>, 1, false>",
+    "normal_f32": "void tk::k_vec_fill<tk::OpNormalF32<false>, 1, false>",
+    "choice_u32": "void tk::k_choice<2, true, false, false>",
+    "philox_u32": "void tk::k_philox_tile<tk::OpPhilox32<false>, false>",
+    "exponential_f64": "void tk::k_exp_fill<tk::OpExpF64, 2, false>",
+    "exponential_f32": "void tk::k_exp_fill<tk::OpExpF32, 2, false>",
+    "calib_copy": "__amd_rocclr_copyBuffer",
+}
+# Algorithmic bytes of each fill's 2^28-element launch (written + read) and the sources its
+# kernel is built from (a traffic record holds only while they are unchanged).
+_FILLS_SRC = ["bulk_fills_amd/csrc/tk_fills.hip", "bulk_fills_amd/csrc/tk_device.h", "bulk_fills_amd/csrc/tk_log.h",
+              "bulk_fills_amd/csrc/logf256.inc", "bulk_fills_amd/csrc/log128.inc", "include/tk_device_api.h"]
+FILL_SOURCES = {k: _FILLS_SRC for k in FILL_KERNELS}
+FILL_SOURCES["normal_f64"] = ["bulk_fills_amd/csrc/tk_ziggurat.hip", "bulk_fills_amd/csrc/zig1024.inc",
+                              "bulk_fills_amd/csrc/tk_device.h", "include/tk_device_api.h"]
+FILL_SOURCES["choice_u32"] = ["bulk_fills_amd/csrc/tk_choice.hip", "bulk_fills_amd/csrc/tk_device.h",
+                              "include/tk_device_api.h"]
+_N28 = 1 << 28
+FILL_BYTES = {"normal_f64": 8 * _N28, "dropout_f32": 8 * _N28, "u64": 8 * _N28, "f64": 8 * _N28, "u32": 4 * _N28,
+              "f16_bits": 2 * _N28, "normal_f32": 4 * _N28, "choice_u32": 4 * _N28, "philox_u32": 4 * _N28,
+              "exponential_f64": 8 * _N28, "exponential_f32": 4 * _N28, "calib_copy": 8 * _N28}
+
+
+def _csv_rows(d, suffix):
+    import csv
+    import glob
+    for f in sorted(glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True)):
+        with open(f, newline="") as fh:
+            yield from csv.DictReader(fh)
+
+
+def _sources_sha(files):
+    import hashlib
+    here = os.path.dirname(os.path.abspath(__file__))
+    h = hashlib.sha256()
+    for f in files:
+        h.update(open(os.path.join(here, f), "rb").read())
+    return h.hexdigest()
+
+
+def trace_summary(d, min_share=0.0005, timed_only=False):
+    """Markdown table of a --kernel-trace run: per kernel and grid size, calls and the
+    duration statistics of its dispatches (End - Start timestamps).  With timed_only, only
+    the dispatches between the two marker launches (the timed steps)."""
+    rows = sorted(_csv_rows(d, "kernel_trace.csv"), key=lambda r: int(r["Start_Timestamp"]))
+    if timed_only:
+        marks = [i for i, r in enumerate(rows) if "OpConst" in r["Kernel_Name"] and int(r["Grid_Size_X"]) == 256]
+        rows = rows[marks[-2] + 1:marks[-1]] if len(marks) >= 2 else []
+    groups = {}
+    for r in rows:
+        grid = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
+        g = groups.setdefault((r["Kernel_Name"], grid), {"d": [], "vgpr": r["VGPR_Count"], "lds": r["LDS_Block_Size"]})
+        g["d"].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    total = sum(sum(g["d"]) for g in groups.values()) or 1.0
+    out = ["| kernel | grid (threads) | calls | avg us | median us | min us | max us | VGPRs | LDS B | share |",
+           "|---|---|---|---|---|---|---|---|---|---|"]
+    for (name, grid), g in sorted(groups.items(), key=lambda kv: -sum(kv[1]["d"])):
+        share = sum(g["d"]) / total
+        if share < min_share:
+            continue
+        d_ = g["d"]
+        out.append(f"| `{name[:110]}` | {grid} | {len(d_)} | {statistics.fmean(d_):.2f} | {statistics.median(d_):.2f} | "
+                   f"{min(d_):.2f} | {max(d_):.2f} | {g['vgpr']} | {g['lds']} | {100 * share:.1f}% |")
+    return "\n".join(out)
+
+
+def _counter_medians(d):
+    """{(kernel, grid): {counter: median value over the dispatches}} from a --pmc run."""
+    vals = {}
+    for r in _csv_rows(d, "counter_collection.csv"):
+        key = (r["Kernel_Name"], int(r["Grid_Size"]))
+        vals.setdefault(key, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    return {k: {c: statistics.median(v) for c, v in cs.items()} for k, cs in vals.items()}
+
+
+def _fill_launch(meds, fill):
+    """The counters of a fill's 2^28-element launch: its kernel's largest grid."""
+    keys = [k for k in meds if k[0].startswith(FILL_KERNELS[fill])]
+    return meds[max(keys, key=lambda k: k[1])] if keys else None
+
+
+def pmc_summary(fetch_dir, write_dir, out_json):
+    """HBM bytes per launch from a FETCH_SIZE run and a WRITE_SIZE run (KiB per dispatch),
+    scaled by what the same counters read for a plain 1 GiB device copy; writes the record
+    bench.py takes `traffic` from and returns a markdown table."""
+    fetch, write = _counter_medians(fetch_dir), _counter_medians(write_dir)
+    cf, cw = _fill_launch(fetch, "calib_copy"), _fill_launch(write, "calib_copy")
+    copy_kib = float(FILL_BYTES["calib_copy"] // 2 // 1024)  # 1 GiB read and 1 GiB written
+    ff, wf = copy_kib / cf["FETCH_SIZE"], copy_kib / cw["WRITE_SIZE"]
+    rec = {"fetch_factor": ff, "write_factor": wf, "calibration": "1 GiB device copy (__amd_rocclr_copyBuffer)",
+           "kernels": {}}
+    out = [f"Calibration: a 1 GiB device copy reads FETCH_SIZE {cf['FETCH_SIZE']:.1f} KiB and WRITE_SIZE "
+           f"{cw['WRITE_SIZE']:.1f} KiB per dispatch: fetch factor {ff:.4f}, write factor {wf:.4f}.", "",
+           "| fill | kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | scaled HBM bytes | algorithmic bytes | ratio |",
+           "|---|---|---|---|---|---|---|"]
+    for fill in FILL_KERNELS:
+        if fill == "calib_copy":
+            continue
+        f_, w_ = _fill_launch(fetch, fill), _fill_launch(write, fill)
+        if not f_ or not w_:
+            continue
+        traffic = f_["FETCH_SIZE"] * 1024 * ff + w_["WRITE_SIZE"] * 1024 * wf
+        algo = FILL_BYTES[fill]
+        rec["kernels"][fill] = {"kernel": FILL_KERNELS[fill], "fetch_kib": f_["FETCH_SIZE"], "write_kib": w_["WRITE_SIZE"],
+                                "traffic_bytes": traffic, "algorithmic_bytes": algo, "sources": FILL_SOURCES[fill],
+                                "source_sha256": _sources_sha(FILL_SOURCES[fill])}
+        out.append(f"| {fill} | `{FILL_KERNELS[fill]}` | {f_['FETCH_SIZE']:.1f} | {w_['WRITE_SIZE']:.1f} | "
+                   f"{traffic:.4g} | {algo:.4g} | {traffic / algo:.4f} |")
+    with open(out_json, "w") as fh:
+        json.dump(rec, fh, indent=1)
+    return "\n".join(out)
+
+
+def counter_summary(d):
+    """Markdown table of the per-dispatch counters of a --pmc run, per fill (median over the
+    fill's 2^28-element dispatches; SQ_* per wave where SQ_WAVES was collected)."""
+    meds = _counter_medians(d)
+    rows = [(f, _fill_launch(meds, f)) for f in FILL_KERNELS if f != "calib_copy"]
+    rows = [(f, c) for f, c in rows if c]
+    names = sorted({k for _, c in rows for k in c})
+    out = ["| fill | " + " | ".join(names) + " |", "|---|" + "---|" * len(names)]
+    for f, c in rows:
+        waves = c.get("SQ_WAVES")
+        cells = []
+        for k in names:
+            v = c.get(k)
+            if v is None:
+                cells.append("")
+            elif waves and k.startswith("SQ_INSTS"):
+                cells.append(f"{v / waves:.1f} / wave")
+            else:
+                cells.append(f"{v:.4g}")
+        out.append(f"| {f} | " + " | ".join(cells) + " |")
+    return "\n".join(out)
 
 
 def parse():
@@ -46,6 +194,13 @@ def parse():
     ap.add_argument("--cpu-single-log2", type=int, default=26,
                     help="elements per fill in the one-core oracle sample (0: skip it)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--trace-summary", metavar="DIR",
+                    help="print the kernel-trace summary of a rocprofv3 --kernel-trace output directory and exit")
+    ap.add_argument("--pmc-summary", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "OUT_JSON"),
+                    help="HBM bytes per launch from FETCH_SIZE and WRITE_SIZE rocprofv3 runs: write the traffic "
+                         "record and print its table, then exit")
+    ap.add_argument("--counter-summary", metavar="DIR",
+                    help="print the per-fill counters of a rocprofv3 --pmc output directory and exit")
     ap.add_argument("--only", default="",
                     help="comma-separated fill names to run (profiling); 'calib_copy' adds a plain 1 GiB "
                          "device copy used to calibrate the HBM byte counters")
@@ -182,7 +337,17 @@ def build_step(tk, torch, n):
                     ("f64", 8 * n, f64), ("f64 tiles=4", 8 * n, tuned(f64, unroll=4)),
                     ("normal_f64 tiles=2", 8 * n, tuned(zig, zig_tiles=2)),
                     ("normal_f64 tiles=4", 8 * n, tuned(zig, zig_tiles=4)),
-                    ("normal_f64 tiles=8", 8 * n, tuned(zig, zig_tiles=8))]
+                    ("normal_f64 tiles=8", 8 * n, tuned(zig, zig_tiles=8)),
+                    # Philox at word offsets 1..3: the LDS tile kernel (default) against the
+                    # overlapping-wave kernel; start 0 is the direct kernel
+                    ("philox_u32 start 0 direct", 4 * n, lambda s: tk.tk_philox_fill_u32(1, 0, n, optr)),
+                    ("philox_u32 start 1 tile", 4 * n, lambda s: tk.tk_philox_fill_u32(1, 1, n, optr)),
+                    ("philox_u32 start 1 overlap", 4 * n,
+                     tuned(lambda s: tk.tk_philox_fill_u32(1, 1, n, optr), philox_lds=0)),
+                    ("philox_u64_below_1000 start 1 tile", 8 * n,
+                     lambda s: tk.tk_philox_fill_u64_below(1, 1, n, 1000, optr)),
+                    ("philox_u64_below_1000 start 1 overlap", 8 * n,
+                     tuned(lambda s: tk.tk_philox_fill_u64_below(1, 1, n, 1000, optr), philox_lds=0))]
     return fills, next_rows, calib, start_rows, ceil_rows, pattern_rows, (out, x, table)
 
 
@@ -387,6 +552,18 @@ def rate(nbytes, ms):
 
 def main():
     args = parse()
+    if args.trace_summary:
+        print("All dispatches:\n")
+        print(trace_summary(args.trace_summary))
+        print("\nThe timed steps only (between the two marker launches):\n")
+        print(trace_summary(args.trace_summary, min_share=0.0, timed_only=True))
+        return
+    if args.pmc_summary:
+        print(pmc_summary(*args.pmc_summary))
+        return
+    if args.counter_summary:
+        print(counter_summary(args.counter_summary))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the fills shard with no communication, so only "
               "--gpus 1 is supported here", file=sys.stderr)
@@ -472,12 +649,16 @@ def main():
     # fill's launch, on the stream it is launched on (torch's current stream), without the
     # system-scope fence torch's events would add
     dev = [{dj: (FenceFreeEvent(tk.lib), FenceFreeEvent(tk.lib))} for _ in range(K)]
+    marker = keep[0].data_ptr()
+    tk.tk_fill_constant_u32(TIMED_MARKER, MARKER_N, marker)  # marks the timed region in a kernel trace
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(K):
         step(s, dev[s])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    tk.tk_fill_constant_u32(TIMED_MARKER, MARKER_N, marker)
+    torch.cuda.synchronize()
 
     elapsed = t1 - t0
     value = bytes_step * K / elapsed / GIB
