@@ -31,7 +31,7 @@ HBM_PEAK_GBS = 8000.0
 # dependent integer steps per lane before each store of the constant fill, swept for the
 # store ceiling (stores spaced by some arithmetic, as in the fills, can go faster than
 # stores issued back to back)
-CONST_WORK = (0, 8, 12, 16, 20, 24, 32, 64)
+CONST_WORK = (0, 8, 12, 16, 20, 24, 28, 32, 64)
 # a constant fill of MARKER_N words (one work-group, a grid no other launch has) right before
 # and right after the timed steps, so that a kernel trace can pick out the timed region
 TIMED_MARKER, MARKER_N = 0x7E57AB1E, 64

@@ -270,6 +270,11 @@ __global__ __launch_bounds__(kB) void k_zig_table_pass(ZigArgs a) {
   if (kFused) {
     if (threadIdx.x == 0 && a.counts) a.counts[blockIdx.x] = seen;
     if (!over) {
+      // Each value here replaces the placeholder a wave of this group stored in its tile
+      // before the barrier.  The barrier does not wait for those stores to complete; the
+      // order comes from the group running on one CU (no tgsplit), whose waves' vector
+      // memory instructions pass through one texture path and L1 in issue order to the L2
+      // channel that owns the address, so this later store lands after the placeholder.
       for (uint32_t j = threadIdx.x; j < kept; j += kB) {
         const uint32_t k = entry(j);
         a.out[k] = zig_slow<kPhilox>(a, k);
