@@ -47,7 +47,7 @@ FILL_KERNELS = {
     "f64": "void tk::k_vec_fill<tk::OpWord64<true>, 1, false>",
     "u32": "void tk::k_vec_fill<tk::OpWord32<false>, 1, false>",
     "f16_bits": "void tk::k_vec_fill<tk::OpSub16<true>, 1, false>",
-    "normal_f32": "void tk::k_vec_fill<tk::OpNormalF32<false>, 1, false>",
+    "normal_f32": "void tk::k_vec_line<tk::OpNormalF32<false>, false>",
     "choice_u32": "void tk::k_choice<2, true, false, false>",
     "philox_u32": "void tk::k_philox_tile<tk::OpPhilox32<false>, false>",
     "exponential_f64": "void tk::k_exp_fill<tk::OpExpF64, 2, false>",
@@ -414,26 +414,31 @@ def measured_traffic(fill):
 
 
 def _oracle_jobs(x):
-    """(bytes written per element, fn(start, n)) for every fill of one step, over the oracle.
+    """(fill name, bytes written per element, fn(start, n)) for every fill of one step, over
+    the oracle.
     x: the dropout input of at least as many elements as the largest call."""
     import oracle
     import tk_inputs as ti
     q, a, _ = oracle.alias_build(ti.zipf_weights())
     L, LB = ti.LOW, ti.LOW_BOUND
     return [
-        (4, lambda s, m: oracle.fill_u32(1, s, m)), (8, lambda s, m: oracle.fill_u64(1, s, m)),
-        (4, lambda s, m: oracle.fill_f32(1, s, m)), (8, lambda s, m: oracle.fill_f64(1, s, m)),
-        (2, lambda s, m: oracle.fill_u16(1, s, m)), (2, lambda s, m: oracle.fill_f16_bits(1, s, m)),
-        (1, lambda s, m: oracle.fill_u8(1, s, m)), (1, lambda s, m: oracle.fill_bool(1, s, m)),
-        (4, lambda s, m: oracle.fill_u32_below(1, s, m, 1000)),
-        (4, lambda s, m: oracle.fill_u32_below(1, s, m, (1 << 32) - 2)),
-        (8, lambda s, m: oracle.fill_u64_below(1, s, m, 1000)),
-        (8, lambda s, m: oracle.fill_u64_below(1, s, m, (1 << 64) - 2)),
-        (4, lambda s, m: oracle.fill_i32_below(1, s, m, L, LB)),
-        (8, lambda s, m: oracle.fill_i64_below32(1, s, m, L, LB)),
-        (8, lambda s, m: oracle.fill_normal_f64(1, s, m)), (4, lambda s, m: oracle.fill_normal_f32(1, s, m)),
-        (4, lambda s, m: oracle.dropout_f32(ti.DROPOUT_KEY, s, x[s:s + m], ti.DROPOUT_P, with_mask=False)),
-        (4, lambda s, m: oracle.fill_choice_u32(1, s, m, q, a)), (4, lambda s, m: oracle.philox_fill_u32(1, s, m)),
+        ("u32", 4, lambda s, m: oracle.fill_u32(1, s, m)), ("u64", 8, lambda s, m: oracle.fill_u64(1, s, m)),
+        ("f32", 4, lambda s, m: oracle.fill_f32(1, s, m)), ("f64", 8, lambda s, m: oracle.fill_f64(1, s, m)),
+        ("u16", 2, lambda s, m: oracle.fill_u16(1, s, m)),
+        ("f16_bits", 2, lambda s, m: oracle.fill_f16_bits(1, s, m)),
+        ("u8", 1, lambda s, m: oracle.fill_u8(1, s, m)), ("bool", 1, lambda s, m: oracle.fill_bool(1, s, m)),
+        ("u32_below_1000", 4, lambda s, m: oracle.fill_u32_below(1, s, m, 1000)),
+        ("u32_below_2^32-2", 4, lambda s, m: oracle.fill_u32_below(1, s, m, (1 << 32) - 2)),
+        ("u64_below_1000", 8, lambda s, m: oracle.fill_u64_below(1, s, m, 1000)),
+        ("u64_below_2^64-2", 8, lambda s, m: oracle.fill_u64_below(1, s, m, (1 << 64) - 2)),
+        ("i32_below_low", 4, lambda s, m: oracle.fill_i32_below(1, s, m, L, LB)),
+        ("i64_below32_low", 8, lambda s, m: oracle.fill_i64_below32(1, s, m, L, LB)),
+        ("normal_f64", 8, lambda s, m: oracle.fill_normal_f64(1, s, m)),
+        ("normal_f32", 4, lambda s, m: oracle.fill_normal_f32(1, s, m)),
+        ("dropout_f32", 4,
+         lambda s, m: oracle.dropout_f32(ti.DROPOUT_KEY, s, x[s:s + m], ti.DROPOUT_P, with_mask=False)),
+        ("choice_u32", 4, lambda s, m: oracle.fill_choice_u32(1, s, m, q, a)),
+        ("philox_u32", 4, lambda s, m: oracle.philox_fill_u32(1, s, m)),
     ]
 
 
@@ -469,11 +474,14 @@ def cpu_baseline(n_full, single_log2):
     jobs = _oracle_jobs(x)
     cut = [(n_full * j) // P for j in range(P + 1)]
     total_bytes, total_s = 0, 0.0
+    per_fill = {}
     with ThreadPoolExecutor(P) as pool:
-        for nb, fn in jobs:
+        for name, nb, fn in jobs:
             t0 = time.perf_counter()
             list(pool.map(lambda j: fn(cut[j], cut[j + 1] - cut[j]) is None, range(P)))
-            total_s += time.perf_counter() - t0
+            dt = time.perf_counter() - t0
+            per_fill[name] = {"all_cores_s": round(dt, 4)}
+            total_s += dt
             total_bytes += nb * n_full
     rec = {"value": round(total_bytes / total_s / GIB, 3), "unit": "GiB/s", "cores": P, "kind": "oracle",
            "sample": f"every fill of one step at the full 2^{int(np.log2(n_full))} elements, each cut into {P} "
@@ -482,14 +490,18 @@ def cpu_baseline(n_full, single_log2):
     if single_log2 > 0:
         m = 1 << single_log2
         b1, s1 = 0, 0.0
-        for nb, fn in jobs:
+        for name, nb, fn in jobs:
             t0 = time.perf_counter()
             fn(0, m)
-            s1 += time.perf_counter() - t0
+            dt = time.perf_counter() - t0
+            # one core's time for the whole 2^n_full fill, scaled from the sample
+            per_fill[name]["single_core_s_scaled"] = round(dt * n_full / m, 3)
+            s1 += dt
             b1 += nb * m
         rec["single_core"] = {"value": round(b1 / s1 / GIB, 3), "unit": "GiB/s", "cores": 1,
                               "sample": f"every fill of one step at 2^{single_log2} elements, one thread "
                                         f"({s1:.1f} s)"}
+    rec["per_fill"] = per_fill
     return rec
 
 

@@ -12,9 +12,10 @@
 // never straddle a vector.  Sub-word draws (u8, u16, f16, bool), Box-Muller pairs at odd
 // starts and Philox blocks at starts that are not a multiple of four straddle by at most
 // one word, pair or block: that piece comes from the next lane through a DPP row shift
-// (wave_shl:1).  The last lane of a wave computes its piece itself, except for Philox,
-// where waves store 63 vectors and lane 63 only feeds lane 62 (k_vec_fill_overlap).  No
-// LDS staging and no extra HBM traffic.
+// (wave_shl:1).  The last lane of a wave computes its piece itself (sub-word draws, on
+// the scalar unit), or takes it from the next wave through LDS (Box-Muller pairs,
+// k_pair_tile; Philox blocks, k_philox_tile, which stages every block in LDS).  No extra
+// HBM traffic.
 #include "tk_device.h"
 #include "tk_internal.h"
 #include "tk_log.h"
@@ -33,6 +34,12 @@ struct FillBase {
   uint64_t nvec;   // whole vectors
   uint32_t tail;   // elements after the last whole vector
   bool overlap;    // k_vec_fill_overlap: lane 63 of a wave only feeds lane 62
+  // Launched as k_vec_line (no tile loop) when the grid covers the output: set by the
+  // arithmetic-heavy ops, for which the loop's per-iteration compares and address updates
+  // cost 4-11 % (MI355X, 2^28 elements: Box-Muller pairs 170 -> 152 us, one normal per
+  // counter 227 -> 210, Philox f64 337 -> 300, u64 below 2^64 - 2 319 -> 308); the
+  // store-bound fills measured the same or 1-2 % faster with the loop.
+  static constexpr bool kLine = false;
   __device__ __forceinline__ void *vec_ptr(uint64_t v) const { return (void *)(out + head + v * E); }
   __device__ __forceinline__ uint64_t vec_draw(uint64_t v) const { return start + head + v * E; }
 };
@@ -85,11 +92,30 @@ __global__ __launch_bounds__(kBlock) void k_vec_fill(Op op, uint64_t ntiles) {
   if (blockIdx.x == 0) write_edges(op);
 }
 
+// One vector per lane, one tile per group, no loop: the grid covers the output.  Every
+// lane computes its vector, also past the end, as in k_vec_fill: the ops' vectors may take
+// a piece from the next lane or read lane 0 of the wave, so all 64 lanes must be active
+// (kLine ops compute from counters only and read no memory).
+template <class Op, bool kNT>
+__global__ __launch_bounds__(kBlock) void k_vec_line(Op op) {
+  const uint64_t v = (uint64_t)blockIdx.x * kBlock + threadIdx.x;
+  const uint4 r = op.vec(v);
+  if (v < op.nvec) store16<kNT>(op.vec_ptr(v), r);
+  if (blockIdx.x == 0) write_edges(op);
+}
+
 template <class Op, int U>
 static void launch_vec_u(const Op &op, hipStream_t stream) {
   const uint64_t per_tile = (uint64_t)kBlock * U;
   uint64_t ntiles = (op.nvec + per_tile - 1) / per_tile;
   uint64_t grid = ntiles ? ntiles : 1;
+  if (U == 1 && Op::kLine && grid <= config().max_blocks && grid <= 0x7FFFFFFFull) {
+    if (config().nt_stores)
+      hipLaunchKernelGGL((k_vec_line<Op, true>), dim3((uint32_t)grid), dim3(kBlock), 0, stream, op);
+    else
+      hipLaunchKernelGGL((k_vec_line<Op, false>), dim3((uint32_t)grid), dim3(kBlock), 0, stream, op);
+    return;
+  }
   if (grid > config().max_blocks) grid = config().max_blocks;
   if (grid > 0x7FFFFFFFull) grid = 0x7FFFFFFFull;
   if (config().nt_stores)
@@ -105,8 +131,8 @@ static void launch_vec_u(const Op &op, hipStream_t stream) {
 // 16-byte vector.  Measured on MI355X (2^28 elements): Philox u32 at start 1 or 2 from
 // ~224 to ~205 us, the Philox normal f32 from ~260 to ~190-205 us.  For lowbias32
 // Box-Muller pairs at odd starts it measured no better than the divergent pair (~208 us
-// either way): a wave span of 1008 bytes alone costs that much, so those stay on
-// k_vec_fill.
+// either way): a wave span of 1008 bytes alone costs that much; those take the pair tile
+// kernel below.
 template <class Op, bool kNT>
 __global__ __launch_bounds__(kBlock) void k_vec_fill_overlap(Op op) {
   const uint64_t wave = (uint64_t)blockIdx.x * (kBlock / 64) + (threadIdx.x >> 6);
@@ -168,6 +194,49 @@ static tk_status launch_philox_tile(const Op &op, hipStream_t stream) {
     hipLaunchKernelGGL((k_philox_tile<Op, true>), dim3((uint32_t)grid), dim3(kBlock), 0, stream, op);
   else
     hipLaunchKernelGGL((k_philox_tile<Op, false>), dim3((uint32_t)grid), dim3(kBlock), 0, stream, op);
+  return launch_status();
+}
+
+// Box-Muller pairs at odd start draws (lowbias32): a vector is sin of pair c0, pair c0+1
+// and cos of pair c0+2, whose cosine is the next lane's first value.  Lanes take it from
+// their neighbour; lane 63 of a wave takes lane 0's of the next wave through LDS; and the
+// last wave computes the first pair of the next tile once (its counter is the same for the
+// whole wave: the hashes run on the scalar unit, the cosine's arithmetic once per group
+// instead of once per wave).  One barrier per group; stores as in the aligned fills.
+template <class Op, bool kNT>
+__global__ __launch_bounds__(kBlock) void k_pair_tile(Op op) {
+  constexpr uint32_t kWaves = kBlock / 64;
+  __shared__ float first[kWaves + 1];
+  const uint64_t v = (uint64_t)blockIdx.x * kBlock + threadIdx.x;
+  const uint32_t c0 = (uint32_t)(op.vec_draw(v) >> 1);
+  float a, b, c, d;
+  op.pair(c0, &a, &b);
+  op.pair(c0 + 1u, &c, &d);
+  const uint32_t wave = (uint32_t)__builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (lane_id() == 0) first[wave] = a;
+  if (wave == kWaves - 1) {
+    const uint32_t cn = (uint32_t)__builtin_amdgcn_readfirstlane(c0) + 128u;  // 64 lanes, 2 pairs each
+    float en, s_unused;
+    op.pair(cn, &en, &s_unused);
+    if (lane_id() == 0) first[kWaves] = en;
+  }
+  float e = from_next_lane(a);
+  __syncthreads();
+  if (lane_id() == 63) e = first[wave + 1];
+  if (v < op.nvec)
+    store16<kNT>(op.vec_ptr(v), make_uint4(__float_as_uint(b), __float_as_uint(c), __float_as_uint(d), __float_as_uint(e)));
+  if (blockIdx.x == 0) write_edges(op);
+}
+
+template <class Op>
+static tk_status launch_pair_tile(const Op &op, hipStream_t stream) {
+  uint64_t grid = (op.nvec + kBlock - 1) / kBlock;
+  if (grid == 0) grid = 1;
+  if (grid > 0x7FFFFFFFull) return TK_EINVAL;
+  if (config().nt_stores)
+    hipLaunchKernelGGL((k_pair_tile<Op, true>), dim3((uint32_t)grid), dim3(kBlock), 0, stream, op);
+  else
+    hipLaunchKernelGGL((k_pair_tile<Op, false>), dim3((uint32_t)grid), dim3(kBlock), 0, stream, op);
   return launch_status();
 }
 
@@ -364,6 +433,7 @@ struct OpBelow32To64 : FillBase<int64_t> {
 // u64 / i64 out from one 64-bit draw per element.
 template <class T, bool kSmall>
 struct OpBelow64 : FillBase<T> {
+  static constexpr bool kLine = !kSmall;  // the 64-bit products of bounds above 2^32
   uint32_t hk, hkp;
   uint64_t s, t;
   int64_t low;
@@ -385,6 +455,7 @@ struct OpBelow64 : FillBase<T> {
 // ---------------------------------------------------------------------------------------
 template <bool kHalfTurn>
 struct OpNormalF32 : FillBase<float> {
+  static constexpr bool kLine = true;
   uint32_t hk;
   // Pair c is the public API's tk_randn2_f32 (or its half-turn form): r = sqrt(-2 ln(1 - u1))
   // with the hardware base-2 logarithm (ln x = ln 2 * log2 x) and square root; cos and sin
@@ -427,6 +498,7 @@ struct OpNormalF32 : FillBase<float> {
 
 // One normal per counter (Phobos, §randn): element i is the cosine of pair i.
 struct OpRandnF32 : FillBase<float> {
+  static constexpr bool kLine = true;
   uint32_t hk;
   __device__ __forceinline__ float elem(uint64_t k) const { return tk_randn_f32(hk, (uint32_t)(start + k)); }
   __device__ __forceinline__ uint4 vec(uint64_t v) const {
@@ -598,6 +670,7 @@ struct OpPhilox32 : FillBase<uint32_t> {
 
 template <bool kFloat>
 struct OpPhilox64 : FillBase<uint64_t> {
+  static constexpr bool kLine = true;
   uint32_t k0, k1;
   __device__ __forceinline__ uint64_t xf(uint32_t lo, uint32_t hi) const {
     if (kFloat) return (uint64_t)__double_as_longlong(unit53_lowbits(lo, hi));
@@ -655,6 +728,7 @@ struct OpPhiloxBelow64 : FillBase<uint64_t> {
 
 // Box-Muller pairs over Philox words (pair c: words 2c and 2c+1), laid out as OpNormalF32.
 struct OpPhiloxNormalF32 : FillBase<float> {
+  static constexpr bool kLine = true;
   uint32_t k0, k1;
   __device__ __forceinline__ void pair(uint64_t c, float *cs, float *sn) const {
     tk_box_muller_f32(philox_word(2 * c, k0, k1), philox_word(2 * c + 1, k0, k1), cs, sn);
@@ -719,6 +793,15 @@ template <class Op, class T>
 tk_status run_simple(Op op, T *out, uint64_t start, uint64_t n, hipStream_t stream) {
   set_geometry(op, out, start, n);
   return launch_vec(op, stream);
+}
+
+// Box-Muller pairs: the plain kernel when vectors start at even draws, else the pair tile
+// kernel (tunable "pair_lds"; the plain kernel then takes the pair after the wave itself).
+template <class Op, class T>
+tk_status run_pairs(Op op, T *out, uint64_t start, uint64_t n, hipStream_t stream) {
+  set_geometry(op, out, start, n);
+  if (((op.start + op.head) & 1u) == 0 || !config().pair_lds) return launch_vec(op, stream);
+  return launch_pair_tile(op, stream);
 }
 
 // Philox fills whose vectors straddle blocks when (start + head) & mask != 0: the tile
@@ -881,7 +964,7 @@ tk_status tk_fill_normal_f32(uint32_t key, uint64_t start_draw, uint64_t n, floa
   TK_PRECHECK(out, kMaxW32);
   OpNormalF32<false> op{};
   op.hk = host_lowbias32(key);
-  return run_simple(op, out, start_draw, n, stream);
+  return run_pairs(op, out, start_draw, n, stream);
 }
 
 tk_status tk_fill_normal_f32_half_turn(uint32_t key, uint64_t start_draw, uint64_t n, float *out,
@@ -889,7 +972,7 @@ tk_status tk_fill_normal_f32_half_turn(uint32_t key, uint64_t start_draw, uint64
   TK_PRECHECK(out, kMaxW32);
   OpNormalF32<true> op{};
   op.hk = host_lowbias32(key);
-  return run_simple(op, out, start_draw, n, stream);
+  return run_pairs(op, out, start_draw, n, stream);
 }
 
 tk_status tk_fill_randn_f32(uint32_t key, uint64_t start_draw, uint64_t n, float *out, hipStream_t stream) {

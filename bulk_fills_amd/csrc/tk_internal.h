@@ -54,6 +54,8 @@ struct Config {
   std::atomic<bool> zig_lds;         // TK_ZIG_TABLE=lds|global: where the table pass gathers the layers
   std::atomic<bool> philox_lds;      // TK_PHILOX=lds|overlap: Philox fills at word offsets 1..3 by the LDS
                                      // tile kernel or the overlapping-wave kernel
+  std::atomic<bool> pair_lds;        // TK_PAIRS=lds|wave: Box-Muller pairs at odd starts by the pair tile
+                                     // kernel (the next wave's first value through LDS) or each wave alone
   std::atomic<int> const_work;       // TK_CONST_WORK: dependent integer steps per lane before each store of
                                      // the constant fill (0: none), to sweep the store ceiling's spacing
 };

@@ -46,6 +46,9 @@ static bool env_tunable(Config &c, const char *name) {
   } else if (!strcmp(name, "philox_lds")) {
     const char *ph = getenv("TK_PHILOX");
     c.philox_lds = !(ph && strcmp(ph, "overlap") == 0);
+  } else if (!strcmp(name, "pair_lds")) {
+    const char *pr = getenv("TK_PAIRS");
+    c.pair_lds = !(pr && strcmp(pr, "wave") == 0);
   } else if (!strcmp(name, "const_work")) {
     const uint64_t w = env_u64("TK_CONST_WORK", 0);
     c.const_work = w > 4096 ? 4096 : (int)w;
@@ -56,7 +59,8 @@ static bool env_tunable(Config &c, const char *name) {
 }
 
 static const char *const kTunables[] = {"store_nt",  "max_blocks", "unroll",  "choice_tiles", "exp_tiles",
-                                        "zig_tiles", "zig_lds",    "zig_fused", "philox_lds", "const_work"};
+                                        "zig_tiles", "zig_lds",    "zig_fused", "philox_lds", "pair_lds",
+                                        "const_work"};
 
 static Config &mutable_config() {
   static Config cfg;
@@ -198,6 +202,7 @@ tk_status tk_debug_set_tunable(const char *name, int64_t value) {
   else if (!strcmp(name, "zig_lds") && one_of({0, 1})) c.zig_lds = value == 1;
   else if (!strcmp(name, "zig_fused") && one_of({0, 1})) c.zig_fused = value == 1;
   else if (!strcmp(name, "philox_lds") && one_of({0, 1})) c.philox_lds = value == 1;
+  else if (!strcmp(name, "pair_lds") && one_of({0, 1})) c.pair_lds = value == 1;
   else if (!strcmp(name, "const_work") && value <= 4096) c.const_work = (int)value;
   else return TK_EINVAL;
   return TK_OK;

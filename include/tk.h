@@ -282,6 +282,10 @@ tk_status tk_debug_device_bytes(uint64_t *bytes);
  *                         (TK_ZIG_MODE; tk_debug_set_normal_f64_mode overrides it)
  *   "philox_lds" 0|1      Philox fills at word offsets 1..3 by the LDS tile kernel (1) or
  *                         the overlapping-wave kernel (0) (TK_PHILOX=lds|overlap)
+ *   "pair_lds" 0|1        lowbias32 Box-Muller fills at odd starts by the pair tile kernel,
+ *                         which passes each wave's first value on through LDS (1), or with
+ *                         every wave computing the value after it itself (0)
+ *                         (TK_PAIRS=lds|wave)
  *   "const_work" 0..4096  dependent integer steps per lane before each store of
  *                         tk_fill_constant_u32 (TK_CONST_WORK; 0 = none): the spacing of
  *                         the store-ceiling measurement

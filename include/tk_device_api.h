@@ -65,22 +65,26 @@ __device__ __forceinline__ double tk_uniform_f64(uint32_t hk, uint32_t i) {
 /* Box-Muller of the f32 uniforms of words w1 and w2 (Phobos, §randn; the pair's second
  * value is r sin): r = sqrt(-2 ln(1 - u1)) from the hardware base-2 logarithm and square
  * root, the angle 2 pi t with t = u2 wrapped into [-1/2, 1/2) through the hardware sine
- * and cosine, which take turns.  Within 1.2e-6 of the exact pair; |x| < 5.65. */
+ * and cosine, which take turns.  Within 1.2e-6 of the exact pair; |x| < 5.65.
+ * Both inputs come from the float 1.m of the word's low 23 bits m, each in one exact
+ * subtraction: 1 - u1 = 2 - 1.m, and t = f - 3/2 where f is 1.m with bit 22 of m
+ * flipped, which is 3/2 + u2 for u2 < 1/2 and 1/2 + u2 otherwise. */
 __device__ __forceinline__ void tk_box_muller_f32(uint32_t w1, uint32_t w2, float *cos_part, float *sin_part) {
-  const float u1 = tk_unit23(w1), u2 = tk_unit23(w2);
-  const float r = __builtin_amdgcn_sqrtf(__builtin_amdgcn_logf(1.0f - u1) * -1.38629436111989061883f);
-  const float t = u2 >= 0.5f ? u2 - 1.0f : u2;
+  const float one_minus_u1 = 2.0f - __uint_as_float((w1 & 0x7FFFFFu) | 0x3F800000u);
+  const float t = __uint_as_float((w2 & 0x7FFFFFu) ^ 0x3FC00000u) - 1.5f;
+  const float r = __builtin_amdgcn_sqrtf(__builtin_amdgcn_logf(one_minus_u1) * -1.38629436111989061883f);
   *cos_part = r * __builtin_amdgcn_cosf(t);
   *sin_part = r * __builtin_amdgcn_sinf(t);
 }
 
 /* The same pair with the angle shifted by half a turn (tandem-sycl, "Design", §Normals):
- * t = u2 - 1/2, so both values are the negation of tk_box_muller_f32's. */
+ * t = u2 - 1/2 (= 1.m - 3/2, exact), so both values are the negation of
+ * tk_box_muller_f32's. */
 __device__ __forceinline__ void tk_box_muller_half_turn_f32(uint32_t w1, uint32_t w2, float *cos_part,
                                                             float *sin_part) {
-  const float u1 = tk_unit23(w1), u2 = tk_unit23(w2);
-  const float r = __builtin_amdgcn_sqrtf(__builtin_amdgcn_logf(1.0f - u1) * -1.38629436111989061883f);
-  const float t = u2 - 0.5f;
+  const float one_minus_u1 = 2.0f - __uint_as_float((w1 & 0x7FFFFFu) | 0x3F800000u);
+  const float t = __uint_as_float((w2 & 0x7FFFFFu) | 0x3F800000u) - 1.5f;
+  const float r = __builtin_amdgcn_sqrtf(__builtin_amdgcn_logf(one_minus_u1) * -1.38629436111989061883f);
   *cos_part = r * __builtin_amdgcn_cosf(t);
   *sin_part = r * __builtin_amdgcn_sinf(t);
 }

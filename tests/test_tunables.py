@@ -114,6 +114,20 @@ def check_philox():
                           oracle.philox_fill_u64_below(PK, s, N, (1 << 63) + 1), f"philox u64_below s={s}")
 
 
+def check_pairs():
+    """Both Box-Muller pair fills at even and odd starts, lengths from one element to several
+    tiles with ragged ends (the last tile's lanes past the end still feed their neighbours)."""
+    for fill, orc in ((tk.tk_fill_normal_f32, oracle.fill_normal_f32),
+                      (tk.tk_fill_normal_f32_half_turn, oracle.fill_normal_f32_half_turn)):
+        for s in (0, 1, 3, 5, 255, (1 << 31) + 1):
+            for n in (1, 2, 5, 1023, 1024, 1025, 4099, N):
+                for off in (0, 1):
+                    b = DevBuf(n, 4, 4 * off)
+                    fill(KEY, s, n, b.ptr)
+                    err = np.max(np.abs(b.host(np.float32).astype(np.float64) - orc(KEY, s, n)))
+                    assert err <= 4e-6, f"{fill.__name__} s={s} n={n} off={off}: {err}"
+
+
 def check_all():
     check_streaming()
     check_choice()
@@ -130,6 +144,7 @@ CASES = [
     ("zig_tiles", 16, check_normal_f64), ("zig_lds", 0, check_normal_f64), ("zig_fused", 0, check_normal_f64),
     ("const_work", 16, check_constant), ("const_work", 200, check_constant),
     ("philox_lds", 0, check_philox), ("philox_lds", 1, check_philox),
+    ("pair_lds", 0, check_pairs), ("pair_lds", 1, check_pairs),
 ]
 
 
