@@ -57,7 +57,7 @@ FILL_KERNELS = {
 # Algorithmic bytes of each fill's 2^28-element launch (written + read) and the sources its
 # kernel is built from (a traffic record holds only while they are unchanged).
 _FILLS_SRC = ["bulk_fills_amd/csrc/tk_fills.hip", "bulk_fills_amd/csrc/tk_device.h", "bulk_fills_amd/csrc/tk_log.h",
-              "bulk_fills_amd/csrc/logf256.inc", "bulk_fills_amd/csrc/log128.inc", "include/tk_device_api.h"]
+              "bulk_fills_amd/csrc/logf256.inc", "bulk_fills_amd/csrc/log256.inc", "include/tk_device_api.h"]
 FILL_SOURCES = {k: _FILLS_SRC for k in FILL_KERNELS}
 FILL_SOURCES["normal_f64"] = ["bulk_fills_amd/csrc/tk_ziggurat.hip", "bulk_fills_amd/csrc/zig1024.inc",
                               "bulk_fills_amd/csrc/tk_device.h", "include/tk_device_api.h"]

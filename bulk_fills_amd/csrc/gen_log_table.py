@@ -1,38 +1,39 @@
-"""Writes log128.inc: the reduction table of the exponential fills' f64 logarithm.
+"""Writes the reduction tables of the exponential fills' logarithms: log256.inc (f64) and
+logf256.inc (f32).
 
-The logarithm is table-driven after Tang (1990, "Table-driven implementation of the
-logarithm function in IEEE floating-point arithmetic", ACM TOMS 16(4)).  For the fills'
-arguments x = 1 - u in (0, 1]:
+Both logarithms reduce after Tang (1990, "Table-driven implementation of the logarithm
+function in IEEE floating-point arithmetic", ACM TOMS 16(4)): for x = 1 - u in (0, 1],
 
-    x = 2^E z,  z in [0.6875, 1.375)             (E <= 0, exact; 7 leading fraction bits of
-                                                  x's mantissa pick the entry j)
-    ln x = E ln 2 + ln c_j + ln(1 + q),   q = (z - c_j) / c_j,  |q| <= 2^-8 (2^-7 at j = 0)
+    x = 2^E z,  z in [0.6875, 1.375)      (the leading fraction bits of x pick entry j)
+    ln x = E ln 2 - ln v_j + ln(1 + q),   q = z v_j - 1,
 
-Entry j covers the mantissas 1 + [j, j+1)/128.  Entries 0..47 take z in [1, 1.375) and
-entries 48..127 halve it into [0.6875, 1).  c_j is the middle of the entry's z interval
-(at most 10 significant bits, so z - c_j is exact), except c_0 = c_127 = 1: the two
-entries next to x = 1 then reduce to ln(1 + q) with q = z - 1 exact, and -ln x keeps its
-relative accuracy for x just below 1 (u near 0), where -ln x ~ u.
+with a multiplier v_j close to 1 / z over the entry.  Giving v_j few significant bits makes
+q exact in one fused multiply-add (the product z v_j has few more bits than z, and its
+leading bits cancel against 1), so neither c_j nor a correction term is read.  The kernels
+keep z in [1, 2) and put the halving into the stored multiplier m_j (z m_j = (z / 2) v_j
+exactly).  v_0 = v_255 = 1: the entries next to x = 1 then reduce to ln(1 + q) with q = z - 1
+exact (after the halving for j = 255), and -ln x keeps its relative accuracy for x just
+below 1 (u near 0), where -ln x ~ u.
 
-Per entry the kernels read four doubles:
-    invc     1 / c_j rounded to nearest
-    nlog_hi  -ln c_j rounded to a multiple of 2^-45
-    nlog_lo  -ln c_j - nlog_hi rounded to nearest
-    c        c_j (exact)
-and ln 2 = LN2_HI + LN2_LO with LN2_HI a multiple of 2^-45, so that
-n LN2_HI + nlog_hi (0 <= n <= 53) is exact in one fused multiply-add.
+f64 (log256.inc).  x = 1 - u on the 2^-53 grid has up to 53 significant bits.  256 entries
+(entry j: z in 1 + [j, j+1)/256, halved into [0.6875, 1) from j = 96 on); v_j has at most 9
+significant bits, chosen to minimise max |q| over the entry, and the generator checks
+|q| < 2^-8 at both ends of every entry, which makes z m_j - 1 exact for every z of it.  Per
+entry 16 bytes:
+    l_hi     ln v_j rounded to a multiple of 2^-45
+    m        the high word of m_j (its low word is zero: 9 significant bits)
+    l_lo     the high word of ln v_j - l_hi rounded to 21 significant bits (low word zero)
+and ln 2 = LN2_HI + LN2_LO with LN2_HI a multiple of 2^-45, so that n LN2_HI + l_hi
+(0 <= n <= 53) is exact in one fused multiply-add.
 
-The f32 exponential has its own table, logf256.inc: its arguments x = k 2^-24 (1 <= k <=
-2^24) have at most 24 significant bits, so with a multiplier v_j of at most 24 significant
-bits the reduction q = z v_j - 1 is exact in one fused multiply-add, and c_j need not be
-read.  256 entries (|q| <= 2^-9, 2^-8 at j = 0), entries 96..255 halve z into
-[0.6875, 1).  The kernel keeps z in [1, 2) and the halving sits in the stored multiplier
-(z (v_j / 2) = (z / 2) v_j exactly); per entry:
+f32 (logf256.inc).  x = k 2^-24 (1 <= k <= 2^24) has at most 24 significant bits, so v_j
+may have 24 and q is still exact.  256 entries (|q| <= 2^-9, 2^-8 at j = 0), halved from
+entry 96 on; per entry
     m        v_j = 1 / c_j rounded to 24 significant bits (1 at j = 0 and j = 255), halved
              for j >= 96: the multiplier of z in [1, 2)
     l        ln v_j rounded to nearest, so that -ln x = n ln 2 + l - ln(1 + q)
 
-Run:  python gen_log_table.py  (rewrites log128.inc and logf256.inc next to this file).
+Run:  python gen_log_table.py  (rewrites log256.inc and logf256.inc next to this file).
 """
 import os
 from fractions import Fraction
@@ -41,17 +42,11 @@ import mpmath as mp
 from mpmath.libmp import to_float
 
 mp.mp.dps = 50
-ENTRIES = 128
-SPLIT = 48  # entries from here on halve z into [0.6875, 1)
 HI_QUANTUM = 45
-
-
-def centre(j):
-    if j in (0, ENTRIES - 1):
-        return Fraction(1)
-    lo = 1 + Fraction(j, ENTRIES)
-    mid = lo + Fraction(1, 2 * ENTRIES)
-    return mid / 2 if j >= SPLIT else mid
+D_ENTRIES = 256
+D_SPLIT = 96  # entries from here on halve z into [0.6875, 1)
+D_VBITS = 9
+D_ZULP = Fraction(1, 1 << 52)  # spacing of z in [1, 2)
 
 
 def split_hi(x):
@@ -60,17 +55,64 @@ def split_hi(x):
     return to_float(hi._mpf_, rnd="n"), to_float((x - hi)._mpf_, rnd="n")
 
 
+def d_interval(j):
+    """The reduced arguments of entry j: [a, b) (b excluded)."""
+    a = 1 + Fraction(j, D_ENTRIES)
+    b = a + Fraction(1, D_ENTRIES)
+    return (a / 2, b / 2) if j >= D_SPLIT else (a, b)
+
+
+def d_max_q(j, v):
+    """max |z v - 1| over the z of entry j (its last z is b less one z spacing)."""
+    a, b = d_interval(j)
+    last = b - (D_ZULP / 2 if j >= D_SPLIT else D_ZULP)
+    return max(abs(a * v - 1), abs(last * v - 1))
+
+
+def round_bits(x, bits):
+    """The mpf x rounded to nearest at `bits` significant bits, as a double (exact)."""
+    with mp.workprec(bits):
+        r = +x
+    return to_float(r._mpf_, rnd="n")
+
+
 def build():
+    """Rows (l_hi, m, l_lo) of the f64 table, and LN2_HI, LN2_LO."""
     rows = []
-    for j in range(ENTRIES):
-        c = centre(j)
-        cf = float(c)
-        assert Fraction(cf) == c
-        invc = float(1 / c)  # Fraction -> float rounds to nearest
-        hi, lo = split_hi(-mp.log(mp.mpf(c.numerator) / c.denominator))
-        rows.append((invc, hi, lo, cf))
+    for j in range(D_ENTRIES):
+        if j in (0, D_ENTRIES - 1):
+            v = Fraction(1)
+        else:
+            a, b = d_interval(j)
+            v0 = round_sig(2 / (a + b), D_VBITS)
+            q0 = quantum(v0, D_VBITS)
+            v = min((v0 + d * q0 for d in range(-2, 3)), key=lambda c: (d_max_q(j, c), c))
+        assert d_max_q(j, v) < Fraction(1, 256), j
+        m = v / 2 if j >= D_SPLIT else v
+        mf = float(m)
+        assert Fraction(mf) == m
+        lv = mp.log(mp.mpf(v.numerator) / v.denominator)
+        hi = mp.nint(lv * mp.mpf(2) ** HI_QUANTUM) / mp.mpf(2) ** HI_QUANTUM
+        rows.append((to_float(hi._mpf_, rnd="n"), mf, round_bits(lv - hi, 21)))
     ln2_hi, ln2_lo = split_hi(mp.log(2))
     return rows, ln2_hi, ln2_lo
+
+
+def quantum(v, bits):
+    """The spacing of `bits`-significant-bit numbers at the Fraction v > 0."""
+    e = 0
+    while v >= 2:
+        v /= 2
+        e += 1
+    while v < 1:
+        v *= 2
+        e -= 1
+    return Fraction(2) ** (e - (bits - 1))
+
+
+def high_word(f):
+    import struct
+    return struct.unpack("<Q", struct.pack("<d", f))[0] >> 32
 
 
 F32_ENTRIES = 256
@@ -127,24 +169,28 @@ def write_f32():
     return path
 
 
-def main():
-    write_f32()
+def write_f64():
     rows, ln2_hi, ln2_lo = build()
-    L = ["// Generated by gen_log_table.py: reduction table of the exponential fills' logarithm",
-         "// (Tang's table-driven method).  Do not edit.",
-         f"#define TK_LOG_ENTRIES {ENTRIES}",
-         f"#define TK_LOG_SPLIT {SPLIT}",
+    L = ["// Generated by gen_log_table.py: reduction table of the f64 exponential's logarithm",
+         "// (arguments on the 2^-53 grid; exact reduction q = z m - 1).  Do not edit.",
+         f"#define TK_LOGD_ENTRIES {D_ENTRIES}",
+         f"#define TK_LOGD_SPLIT {D_SPLIT}",
          f"#define TK_LN2_HI {ln2_hi.hex()}",
          f"#define TK_LN2_LO {ln2_lo.hex()}",
-         "// {1 / c, -ln c (multiple of 2^-45), rest of -ln c, c}",
-         "#define TK_LOG_TABLE_ROWS \\"]
-    for invc, hi, lo, c in rows:
-        L.append(f"  {{{invc.hex()}, {hi.hex()}, {lo.hex()}, {c.hex()}}}, \\")
+         "// {l_hi = ln v (multiple of 2^-45), high word of m = v (halved from entry TK_LOGD_SPLIT on),",
+         "//  high word of l_lo = ln v - l_hi (21 significant bits)}; v has at most 9 significant bits",
+         "#define TK_LOGD_TABLE_ROWS \\"]
+    for hi, m, lo in rows:
+        L.append(f"  {{{hi.hex()}, 0x{high_word(m):08X}u, 0x{high_word(lo):08X}u}}, \\")
     L.append("")
-    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "log128.inc")
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "log256.inc")
     with open(path, "w") as f:
         f.write("\n".join(L) + "\n")
     return path
+
+
+def main():
+    return write_f32(), write_f64()
 
 
 if __name__ == "__main__":

@@ -510,26 +510,23 @@ struct OpRandnF32 : FillBase<float> {
 
 // ---------------------------------------------------------------------------------------
 // Exponentials: x = -ln(1 - u), +0 at u = 0, by inversion of the uniform draw.  1 - u is
-// exact in f64 for both types and the logarithm is tk_log.h's (at most 0.514 ulp); the
-// f32 fill rounds it once, which gives the correctly rounded f32 at every point of its
-// 2^-24 grid.
+// exact for both types and the logarithms are tk_log.h's: the f64 one within 0.502 ulp, the
+// f32 one rounded once to the correctly rounded f32 at every point of its 2^-24 grid.
 // ---------------------------------------------------------------------------------------
 // f64: u = (d & (2^53 - 1)) 2^-53 of the 64-bit draw.
 struct OpExpF64 : FillBase<uint64_t> {
-  using Entry = LogEntry;
-  static constexpr int kEntries = TK_LOG_ENTRIES;
-  __device__ static const Entry *table() { return kLogTable; }
+  using Entry = LogEntryD;
+  static constexpr int kEntries = TK_LOGD_ENTRIES;
+  __device__ static const Entry *table() { return kLogTableD; }
   uint32_t hk;
-  __device__ __forceinline__ uint64_t one(uint32_t lo, uint32_t hi, const LogEntry *tab) const {
-    return (uint64_t)__double_as_longlong(neg_ln_unit(1.0 - unit53_lowbits(lo, hi), tab));
-  }
   __device__ __forceinline__ uint64_t elem(uint64_t k) const {
     const uint32_t c = 2u * (uint32_t)(start + k);
-    return one(word(hk, c), word(hk, c + 1), kLogTable);
+    return (uint64_t)__double_as_longlong(neg_ln_draw53(word(hk, c), word(hk, c + 1), kLogTableD));
   }
-  __device__ __forceinline__ uint4 vec(uint64_t v, const LogEntry *tab) const {
+  __device__ __forceinline__ uint4 vec(uint64_t v, const LogEntryD *tab) const {
     const uint32_t c = 2u * (uint32_t)vec_draw(v);
-    const uint64_t a = one(word(hk, c), word(hk, c + 1), tab), b = one(word(hk, c + 2), word(hk, c + 3), tab);
+    const uint64_t a = (uint64_t)__double_as_longlong(neg_ln_draw53(word(hk, c), word(hk, c + 1), tab));
+    const uint64_t b = (uint64_t)__double_as_longlong(neg_ln_draw53(word(hk, c + 2), word(hk, c + 3), tab));
     return u4(lo32(a), hi32(a), lo32(b), hi32(b));
   }
 };

@@ -1,57 +1,77 @@
-// tk_log.h -- -ln x for x in (0, 1], the logarithm of the exponential fills.
+// tk_log.h -- the logarithms of the exponential fills: -ln x for x = 1 - u in (0, 1].
 //
-// Table-driven after Tang (1990, ACM TOMS 16(4)); the table and its derivation are in
-// log128.inc and gen_log_table.py.  For x = 2^E z with z in [0.6875, 1.375):
-//     -ln x = -E ln 2 - ln c_j - ln(1 + q),   q = (z - c_j) / c_j,  |q| <= 2^-8 (2^-7 at j = 0)
-// q is carried as qh + ql (z - c_j is exact, and so is its residual after the product by
-// 1/c_j), ln(1 + q) - q is its Taylor polynomial through q^7 (the next term is below
-// 2^-59 of the result), -E ln 2 - ln c_j is split so that its high part is exact, and the
-// high sum is made exact with Fast2Sum (|w| >= |qh| whenever w != 0).  Over all 2^24
-// points of the 2^-24 grid and 2^26 random points of the 2^-53 grid the error is at most
-// 0.514 ulp, and rounding it to f32 gives the correctly rounded f32 at every grid point.
-// About 30 VALU operations and two 16-byte table reads; the compiler's log takes ~115.
-// The fills read the table from an LDS copy per work-group: as L1 gathers the reads kept
-// the texture addresser ~95 % busy (rocprofv3 TA_TA_BUSY) and bounded both fills.
+// Both reduce after Tang (1990, ACM TOMS 16(4)) with a short multiplier per table entry,
+// so that the reduced argument is exact after one fused multiply-add:
+//     x = 2^-n z' (z' in [0.6875, 1.375)),  -ln x = n ln 2 + ln v_j - ln(1 + q),
+//     q = z' v_j - 1,
+// where z' is z in [1, 2) (the mantissa) or, from the entry that starts at 1.375 on, z / 2,
+// and the kernels compute q as z m_j - 1 with the halving folded into the stored m_j.  The
+// tables and their derivation are in gen_log_table.py (log256.inc for f64, logf256.inc for
+// f32).  The fills read them from an LDS copy per work-group: as L1 gathers the reads kept
+// the texture addresser ~95 % busy (rocprofv3 TA_TA_BUSY) and bounded the fills.
 #pragma once
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "log128.inc"
+#include "log256.inc"
 #include "logf256.inc"
 
 namespace tk {
 
-struct LogEntry {
-  double invc, nlog_hi, nlog_lo, c;  // 1 / c_j, -ln c_j = nlog_hi + nlog_lo, c_j
+// f64: one 16-byte entry per 1/256 of the mantissa range.
+struct LogEntryD {
+  double l_hi;       // ln v_j, a multiple of 2^-45
+  uint32_t m_hi;     // high word of the multiplier m_j (9 significant bits: low word zero)
+  uint32_t l_lo_hi;  // high word of ln v_j - l_hi (21 significant bits: low word zero)
 };
+static_assert(sizeof(LogEntryD) == 16, "one 16-byte LDS read per element");
 
-static __constant__ LogEntry kLogTable[TK_LOG_ENTRIES] = {TK_LOG_TABLE_ROWS};
+static __constant__ LogEntryD kLogTableD[TK_LOGD_ENTRIES] = {TK_LOGD_TABLE_ROWS};
 
-// -ln x for x in [2^-53, 1] (every 1 - u of the fills); exactly +0 at x = 1.  `tab` is
-// kLogTable or a work-group's LDS copy of it.
-__device__ __forceinline__ double neg_ln_unit(double x, const LogEntry *tab) {
-  const uint32_t xh = (uint32_t)__double2hiint(x);
-  const uint32_t j = (xh >> 13) & (TK_LOG_ENTRIES - 1);  // 7 leading fraction bits
-  const bool half = j >= TK_LOG_SPLIT;
-  const int32_t n = 1023 - (int32_t)(xh >> 20) - (half ? 1 : 0);  // -E, 0 <= n <= 53
-  const uint32_t zh = (xh & 0x000FFFFFu) | (half ? 0x3FE00000u : 0x3FF00000u);
-  const double z = __hiloint2double((int)zh, __double2loint(x));
-  const LogEntry t = tab[j];
-  const double f = z - t.c;                                   // exact
-  const double qh = f * t.invc;
-  const double ql = __builtin_fma(-qh, t.c, f) * t.invc;      // the residual is exact
-  double s = __builtin_fma(1.0 / 7, qh, -1.0 / 6);            // ln(1+q) - q = q^2 s(q)
-  s = __builtin_fma(s, qh, 1.0 / 5);
-  s = __builtin_fma(s, qh, -0.25);
-  s = __builtin_fma(s, qh, 1.0 / 3);
-  s = __builtin_fma(s, qh, -0.5);
-  const double p = (qh * qh) * s;
+static_assert(TK_LOGD_ENTRIES == 256 && TK_LOGD_SPLIT == 96, "index bits and the halving threshold below");
+
+// -ln(1 - u) for the f64 exponential, u = (hi & (2^21 - 1)) 2^-21 + lo 2^-53 (the draw's low
+// 53 bits); exactly +0 at u = 0.
+//  - x 2^21 = B - lo 2^-32 with B = 2^21 - (hi & (2^21 - 1)) in [1, 2^21]: one fused
+//    multiply-add of two exact conversions, exact (x 2^53 is an integer of at most 53 bits);
+//  - n = 21 - e (20 - e for the halved entries, e the exponent of x 2^21, 0 <= n <= 53) in
+//    one subtraction: the borrow out of the 20 fraction bits of the high word is the halving
+//    test (fraction bits >= 0x60000), as in the f32 logarithm below;
+//  - q = z m_j - 1 is exact: m_j has at most 9 significant bits and |q| < 2^-8, so the
+//    exact value fits in 53 bits;
+//  - ln(1 + q) - q = q^2 s(q), s the Taylor polynomial through q^5 (ln(1 + q) through q^7;
+//    the next term is below 2^-59 of the result); w = n LN2_HI + l_hi is exact, w - q is
+//    carried exactly as rh + rl (Fast2Sum: |w| >= |q| whenever w != 0), and the low parts
+//    go in last.
+// A CPU model of these operations (tests) finds at most 0.502 ulp of error over every point
+// of the 2^-24 grid and 2^25 more points of the 2^-53 grid, and exact reductions throughout.
+// 20 f64 operations, where the general Tang reduction (z - c_j, a product by 1 / c_j and its
+// residual) with the conversion of u took 27.
+__device__ __forceinline__ double neg_ln_draw53(uint32_t lo, uint32_t hi, const LogEntryD *tab) {
+  const uint32_t b = 0x200000u - (hi & 0x1FFFFFu);
+  const double xs = __builtin_fma((double)lo, -0x1p-32, (double)b);  // x 2^21, exact
+  const uint32_t xh = (uint32_t)__double2hiint(xs);
+  const uint32_t j = (xh >> 12) & 0xFFu;
+  const int32_t n = (int32_t)((((1044u << 20) | 0x5FFFFu) - xh) >> 20);
+  // z in [1, 2): x 2^21's fraction bits under the exponent of 1 (v_bitop3 0xEA = (a & b) | c)
+  const uint32_t zh = __builtin_amdgcn_bitop3_b32(xh, 0x000FFFFFu, 0x3FF00000u, 0xEA);
+  const double z = __hiloint2double((int)zh, __double2loint(xs));
+  const LogEntryD t = tab[j];
+  const double m = __hiloint2double((int)t.m_hi, 0);
+  const double l_lo = __hiloint2double((int)t.l_lo_hi, 0);
+  const double q = __builtin_fma(z, m, -1.0);  // exact
+  double s = __builtin_fma(1.0 / 7, q, -1.0 / 6);
+  s = __builtin_fma(s, q, 1.0 / 5);
+  s = __builtin_fma(s, q, -0.25);
+  s = __builtin_fma(s, q, 1.0 / 3);
+  s = __builtin_fma(s, q, -0.5);
+  const double p = (q * q) * s;
   const double dn = (double)n;
-  const double w = __builtin_fma(dn, TK_LN2_HI, t.nlog_hi);   // exact
-  const double rh = w - qh;
-  const double rl = (w - rh) - qh;                            // exact
-  const double tail = ((__builtin_fma(dn, TK_LN2_LO, t.nlog_lo) - ql) - p) + rl;
+  const double w = __builtin_fma(dn, TK_LN2_HI, t.l_hi);  // exact
+  const double rh = w - q;
+  const double rl = (w - rh) - q;  // exact
+  const double tail = (__builtin_fma(dn, TK_LN2_LO, l_lo) - p) + rl;
   return rh + tail;
 }
 
@@ -65,7 +85,7 @@ __device__ __forceinline__ double neg_ln_unit(double x, const LogEntry *tab) {
 //     -ln x = n ln 2 + ln v_j - ln(1 + q),   ln(1 + q) = q (1 - q/2 + q^2/3 - q^3/4),
 // |q| <= 2^-9 (2^-8 at j = 0), n = 24 - e (23 - e for the halved entries), evaluated as
 // fma(-q, u, w) with u the degree-3 factor and w = n ln 2 + ln v_j: nine f64 operations,
-// where the general logarithm above takes about 25.  n comes from one subtraction: the
+// where the f64 logarithm above takes seventeen.  n comes from one subtraction: the
 // borrow out of the 20 fraction bits of k's high word is exactly the halving test (fraction
 // bits >= 0x60000).  A CPU model of exactly these operations over all 2^24 inputs (tests)
 // gives the correctly rounded f32 at every one, the worst error being 0.28 of the distance

@@ -1,16 +1,17 @@
-"""Host checks of the exponential fills' logarithm tables (log128.inc, logf256.inc), against
-mpmath, and of the f32 exponential's arithmetic over every one of its inputs.
+"""Host checks of the exponential fills' logarithm tables (log256.inc, logf256.inc), against
+mpmath, and of the logarithms' arithmetic (host models of the kernels' operations).
 
 The tables are product data (the kernels read them; the oracle uses the C library's log).
-These tests check the properties the device logarithms' error bounds rest on: for the f64
-table every c_j exact with few bits, z - c_j inside the bound on |q|, 1/c_j rounded to
-nearest, -ln c_j = hi + lo to far beyond double precision with hi on the 2^-45 grid, the
-ln 2 split; for the f32 table multipliers of at most 24 significant bits (so the reduction
-is exact), |q| inside its bound and ln v rounded to nearest; and that both files are what
-their generator writes.  A host model of the f32 logarithm's operations then shows the
-correctly rounded f32 at all 2^24 inputs."""
+These tests check the properties the device logarithms' error bounds rest on: multipliers
+with few enough significant bits that the reduction q = z m - 1 is exact (9 for f64, whose
+z has 53; 24 for f32, whose z has 24), |q| inside its bound at both ends of every entry,
+ln v to the stated precision (f64: hi on the 2^-45 grid plus a 21-bit low part; f32: rounded
+to nearest), the ln 2 split, and that both files are what their generator writes.  Host
+models of the two logarithms then show the f32 one correctly rounded at all 2^24 inputs
+and the f64 one within 0.51 ulp with exact reductions."""
 import os
 import re
+import struct
 from fractions import Fraction
 
 import subprocess
@@ -19,76 +20,92 @@ import mpmath as mp
 import pytest
 
 CSRC = os.path.join(os.path.dirname(__file__), "..", "bulk_fills_amd", "csrc")
-INC = os.path.join(CSRC, "log128.inc")
+INC = os.path.join(CSRC, "log256.inc")
 INC_F = os.path.join(CSRC, "logf256.inc")
 HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def high_word_double(w):
+    return struct.unpack("<d", struct.pack("<Q", int(w, 16) << 32))[0]
 
 
 def parse():
     text = open(INC).read()
     defs = dict(re.findall(r"#define (TK_\w+) (\S+)\n", text))
-    rows = [tuple(float.fromhex(v) for v in m)
-            for m in re.findall(r"\{(\S+), (\S+), (\S+), (\S+)\}", text)]
+    rows = [(float.fromhex(h), high_word_double(m), high_word_double(lo))
+            for h, m, lo in re.findall(r"\{(\S+), 0x([0-9A-F]+)u, 0x([0-9A-F]+)u\}", text)]
     return defs, rows
 
 
-def z_interval(j, entries, split):
-    lo = 1 + Fraction(j, entries)
-    hi = lo + Fraction(1, entries)
-    return (lo / 2, hi / 2) if j >= split else (lo, hi)
-
-
-def test_shape_and_constants():
-    defs, rows = parse()
-    entries, split = int(defs["TK_LOG_ENTRIES"]), int(defs["TK_LOG_SPLIT"])
-    assert len(rows) == entries == 128
-    mp.mp.dps = 60
-    hi, lo = float.fromhex(defs["TK_LN2_HI"]), float.fromhex(defs["TK_LN2_LO"])
-    assert (Fraction(hi) * 2 ** 45).denominator == 1
-    assert abs(mp.mpf(hi) + mp.mpf(lo) - mp.log(2)) < mp.mpf(2) ** -100
-    # the reduction covers [0.6875, 1.375): entry 47 ends at 1.375, entry 48 starts at 0.6875
-    assert z_interval(split - 1, entries, split)[1] == Fraction(11, 8)
-    assert z_interval(split, entries, split)[0] == Fraction(11, 16)
-
-
-def test_entries():
-    defs, rows = parse()
-    entries, split = int(defs["TK_LOG_ENTRIES"]), int(defs["TK_LOG_SPLIT"])
-    mp.mp.dps = 60
-    for j, (invc, nhi, nlo, c) in enumerate(rows):
-        C = Fraction(c)
-        a, b = z_interval(j, entries, split)
-        # c has at most 10 significant bits and lies in the entry's binade, so z - c is exact
-        assert (C * 2 ** 9 * (2 if C < 1 else 1)).denominator == 1, j
-        assert (C < 1) == (j >= split) or C == 1
-        # |q| = |z - c| / c within 2^-8, or 2^-7 at the first entry (c = 1 next to x = 1)
-        q = max(abs(a - C), abs(b - C)) / C
-        assert q <= Fraction(1, 128 if j == 0 else 256), (j, float(q))
-        if j in (0, entries - 1):
-            assert C == 1 and invc == 1.0 and nhi == 0.0 and nlo == 0.0
-        assert invc == float(1 / C)  # Fraction -> float rounds to nearest
-        assert (Fraction(nhi) * 2 ** 45).denominator == 1
-        exact = -mp.log(mp.mpf(C.numerator) / C.denominator)
-        assert abs(mp.mpf(nhi) + mp.mpf(nlo) - exact) <= mp.mpf(2) ** -98, j
-        assert abs(nlo) <= 2.0 ** -46
-
-
-def test_fma_high_part_is_exact():
-    """n ln2_hi + nlog_hi (0 <= n <= 53) needs at most 53 significant bits, so the kernels'
-    single fused multiply-add computes it exactly."""
-    defs, rows = parse()
-    hi = Fraction(float.fromhex(defs["TK_LN2_HI"]))
-    for n in range(54):
-        for _, nhi, _, _ in rows:
-            s = n * hi + Fraction(nhi)
-            assert Fraction(float(s)) == s, (n, nhi)
-
-
-def test_file_matches_generator(tmp_path):
+def generator():
     import importlib.util
     spec = importlib.util.spec_from_file_location("gen_log_table", os.path.join(CSRC, "gen_log_table.py"))
     gen = importlib.util.module_from_spec(spec)
     spec.loader.exec_module(gen)
+    return gen
+
+
+def test_shape_and_constants():
+    defs, rows = parse()
+    entries, split = int(defs["TK_LOGD_ENTRIES"]), int(defs["TK_LOGD_SPLIT"])
+    assert len(rows) == entries == 256 and split == 96
+    # the kernel's halving test: fraction bits of the high word >= split << 12, which the
+    # borrow of (((1044 << 20) | 0x5FFFF) - xh) >> 20 takes (tk_log.h)
+    assert (split << 12) - 1 == 0x5FFFF
+    mp.mp.dps = 60
+    hi, lo = float.fromhex(defs["TK_LN2_HI"]), float.fromhex(defs["TK_LN2_LO"])
+    assert (Fraction(hi) * 2 ** 45).denominator == 1
+    assert abs(mp.mpf(hi) + mp.mpf(lo) - mp.log(2)) < mp.mpf(2) ** -100
+    # the halved entries cover [0.6875, 1): entry 96 starts at 1.375 before the halving
+    assert 1 + Fraction(split, entries) == Fraction(11, 8)
+
+
+def sig_bits(x):
+    f = abs(Fraction(x))
+    while f.denominator != 1:
+        f *= 2
+    n = f.numerator
+    while n and n % 2 == 0:
+        n //= 2
+    return n.bit_length()
+
+
+def test_entries():
+    """Per entry: m has at most 9 significant bits, so z m (z with 53) has at most 62 and
+    z m - 1 with |q| < 2^-8 fits in 53: exact.  |q| is checked at the entry's first z and
+    its last (z on the 2^-52 grid of [1, 2)); ln v to 2^-66 by l_hi + l_lo."""
+    defs, rows = parse()
+    entries, split = int(defs["TK_LOGD_ENTRIES"]), int(defs["TK_LOGD_SPLIT"])
+    mp.mp.dps = 60
+    for j, (l_hi, m, l_lo) in enumerate(rows):
+        assert sig_bits(m) <= 9, j
+        a = 1 + Fraction(j, entries)
+        last = a + Fraction(1, entries) - Fraction(1, 1 << 52)
+        q = max(abs(a * Fraction(m) - 1), abs(last * Fraction(m) - 1))
+        assert q < Fraction(1, 256), (j, float(q))
+        v = Fraction(m) * (2 if j >= split else 1)
+        if j in (0, entries - 1):
+            assert v == 1 and l_hi == 0.0 and l_lo == 0.0
+        assert (Fraction(l_hi) * 2 ** 45).denominator == 1
+        assert sig_bits(l_lo) <= 21
+        exact = mp.log(mp.mpf(v.numerator) / v.denominator)
+        assert abs(mp.mpf(l_hi) + mp.mpf(l_lo) - exact) <= mp.mpf(2) ** -66, j
+        assert abs(l_lo) <= 2.0 ** -46
+
+
+def test_fma_high_part_is_exact():
+    """n LN2_HI + l_hi (0 <= n <= 53) needs at most 53 significant bits, so the kernel's
+    single fused multiply-add computes it exactly."""
+    defs, rows = parse()
+    hi = Fraction(float.fromhex(defs["TK_LN2_HI"]))
+    for n in range(54):
+        for l_hi, _, _ in rows:
+            s = n * hi + Fraction(l_hi)
+            assert Fraction(float(s)) == s, (n, l_hi)
+
+
+def test_file_matches_generator():
+    gen = generator()
     rows, ln2_hi, ln2_lo = gen.build()
     defs, parsed = parse()
     assert parsed == rows
@@ -96,21 +113,23 @@ def test_file_matches_generator(tmp_path):
     assert parse_f()[1] == gen.build_f32()
 
 
+def test_f64_logarithm_model(tmp_path):
+    """The host model of the f64 logarithm: within 0.51 ulp of -ln(1 - u) over the 2^-24 grid
+    and 2^25 points of the 2^-53 grid, every reduction exact, +0 at u = 0."""
+    exe = str(tmp_path / "exp_f64_model")
+    subprocess.run(["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-I", CSRC, "-o", exe,
+                    os.path.join(HERE, "exp_f64_model.c"), "-lm"], check=True)
+    worst, inexact, wrong_zero = subprocess.run([exe], check=True, capture_output=True, text=True).stdout.split()
+    assert int(inexact) == 0
+    assert int(wrong_zero) == 0
+    assert float(worst) < 0.51, worst
+
+
 def parse_f():
     text = open(INC_F).read()
     defs = dict(re.findall(r"#define (TK_\w+) (\S+)\n", text))
     rows = [tuple(float.fromhex(v) for v in m) for m in re.findall(r"\{(\S+), (\S+)\}", text)]
     return defs, rows
-
-
-def sig_bits(x):
-    f = Fraction(x)
-    while f.denominator != 1:
-        f *= 2
-    n = f.numerator
-    while n % 2 == 0:
-        n //= 2
-    return n.bit_length()
 
 
 def test_f32_table_entries():
