@@ -30,8 +30,10 @@ GIB = float(1 << 30)
 HBM_PEAK_GBS = 8000.0
 # dependent integer steps per lane before each store of the constant fill, swept for the
 # store ceiling (stores spaced by some arithmetic, as in the fills, can go faster than
-# stores issued back to back)
-CONST_WORK = (0, 8, 12, 16, 20, 24, 28, 32, 64)
+# stores issued back to back), and dynamic LDS per work-group (fewer groups in flight per
+# compute unit can also write faster)
+CONST_WORK = (0, 12, 24, 32)
+CONST_LDS = (0, 32768, 49152)
 # a constant fill of MARKER_N words (one work-group, a grid no other launch has) right before
 # and right after the timed steps, so that a kernel trace can pick out the timed region
 TIMED_MARKER, MARKER_N = 0x7E57AB1E, 64
@@ -302,18 +304,21 @@ def build_step(tk, torch, n):
         rc = hip.hipMemsetAsync(optr, 0, nb, torch.cuda.current_stream().cuda_stream)
         if rc != 0:
             raise RuntimeError(f"hipMemsetAsync failed: hipError {rc}")
-    def const_fill(nb, work):
+    def const_fill(nb, work, lds):
         def f(s):
             tk.tk_debug_set_tunable("const_work", work)
+            tk.tk_debug_set_tunable("lds_pad", lds)
             try:
                 tk.tk_fill_constant_u32(0, nb // 4, optr)
             finally:
                 tk.tk_debug_set_tunable("const_work", -1)
+                tk.tk_debug_set_tunable("lds_pad", -1)
         return f
     ceil_rows = []
     for nb in (n, 2 * n, 4 * n, 8 * n):
         for work in CONST_WORK:
-            ceil_rows.append((f"constant_fill_work{work}", nb, const_fill(nb, work)))
+            for lds in CONST_LDS:
+                ceil_rows.append((f"constant_fill_work{work}_lds{lds >> 10}k", nb, const_fill(nb, work, lds)))
         ceil_rows.append(("hipMemsetAsync", nb, (lambda nb: lambda s: memset(nb))(nb)))
     # the store pattern, 2 GiB: consecutive 4 KiB tiles per work-group (one, two or four),
     # a capped grid whose groups stride over the output, for the constant fill, the f64
@@ -335,6 +340,11 @@ def build_step(tk, torch, n):
                     ("constant_fill tiles=4", 8 * n, tuned(c2, unroll=4)),
                     ("constant_fill grid=8192", 8 * n, tuned(c2, max_blocks=8192)),
                     ("f64", 8 * n, f64), ("f64 tiles=4", 8 * n, tuned(f64, unroll=4)),
+                    # the integer fills' LDS cap on resident groups against none
+                    ("u64", 8 * n, lambda s: tk.tk_fill_u64(1, 0, n, optr)),
+                    ("u64 uncapped", 8 * n, tuned(lambda s: tk.tk_fill_u64(1, 0, n, optr), lds_pad=0)),
+                    ("u32", 4 * n, lambda s: tk.tk_fill_u32(1, 0, n, optr)),
+                    ("u32 uncapped", 4 * n, tuned(lambda s: tk.tk_fill_u32(1, 0, n, optr), lds_pad=0)),
                     ("normal_f64 tiles=2", 8 * n, tuned(zig, zig_tiles=2)),
                     ("normal_f64 tiles=4", 8 * n, tuned(zig, zig_tiles=4)),
                     ("normal_f64 tiles=8", 8 * n, tuned(zig, zig_tiles=8)),

@@ -296,7 +296,7 @@ def tk_debug_set_normal_f64_mode(mode):
 
 
 TUNABLES = ("store_nt", "max_blocks", "unroll", "choice_tiles", "exp_tiles", "zig_tiles", "zig_lds", "zig_fused",
-            "philox_lds", "pair_lds", "const_work")
+            "philox_lds", "pair_lds", "lds_pad", "zig_lds_pad", "const_work")
 
 
 def tk_debug_set_tunable(name, value):

@@ -40,6 +40,13 @@ struct FillBase {
   // counter 227 -> 210, Philox f64 337 -> 300, u64 below 2^64 - 2 319 -> 308); the
   // store-bound fills measured the same or 1-2 % faster with the loop.
   static constexpr bool kLine = false;
+  // Dynamic LDS per work-group, which caps the groups a compute unit holds (160 KiB of
+  // LDS): the store-bound integer fills write faster with fewer groups in flight (MI355X,
+  // 2^28 elements, alternating rounds: u32 155.5 -> 150.6 us and u64 308.5 -> 296.7 at
+  // 32 KiB, five groups per compute unit; f64 299.4 -> 296.4 at 24 KiB), while the fills with
+  // more arithmetic per store, or a load, lose time without the latency hiding of a full
+  // compute unit (Box-Muller, Philox, exponentials, dropout: 0).
+  static constexpr uint32_t kLdsPad = 0;
   __device__ __forceinline__ void *vec_ptr(uint64_t v) const { return (void *)(out + head + v * E); }
   __device__ __forceinline__ uint64_t vec_draw(uint64_t v) const { return start + head + v * E; }
 };
@@ -111,17 +118,17 @@ static void launch_vec_u(const Op &op, hipStream_t stream) {
   uint64_t grid = ntiles ? ntiles : 1;
   if (U == 1 && Op::kLine && grid <= config().max_blocks && grid <= 0x7FFFFFFFull) {
     if (config().nt_stores)
-      hipLaunchKernelGGL((k_vec_line<Op, true>), dim3((uint32_t)grid), dim3(kBlock), 0, stream, op);
+      hipLaunchKernelGGL((k_vec_line<Op, true>), dim3((uint32_t)grid), dim3(kBlock), lds_pad<Op>(), stream, op);
     else
-      hipLaunchKernelGGL((k_vec_line<Op, false>), dim3((uint32_t)grid), dim3(kBlock), 0, stream, op);
+      hipLaunchKernelGGL((k_vec_line<Op, false>), dim3((uint32_t)grid), dim3(kBlock), lds_pad<Op>(), stream, op);
     return;
   }
   if (grid > config().max_blocks) grid = config().max_blocks;
   if (grid > 0x7FFFFFFFull) grid = 0x7FFFFFFFull;
   if (config().nt_stores)
-    hipLaunchKernelGGL((k_vec_fill<Op, U, true>), dim3((uint32_t)grid), dim3(kBlock), 0, stream, op, ntiles);
+    hipLaunchKernelGGL((k_vec_fill<Op, U, true>), dim3((uint32_t)grid), dim3(kBlock), lds_pad<Op>(), stream, op, ntiles);
   else
-    hipLaunchKernelGGL((k_vec_fill<Op, U, false>), dim3((uint32_t)grid), dim3(kBlock), 0, stream, op, ntiles);
+    hipLaunchKernelGGL((k_vec_fill<Op, U, false>), dim3((uint32_t)grid), dim3(kBlock), lds_pad<Op>(), stream, op, ntiles);
 }
 
 // Philox fills at word offsets that are not a multiple of four, whose vector needs the head
@@ -151,9 +158,9 @@ static tk_status launch_vec_overlap(Op op, hipStream_t stream) {
   if (grid == 0) grid = 1;
   if (grid > 0x7FFFFFFFull) return TK_EINVAL;
   if (config().nt_stores)
-    hipLaunchKernelGGL((k_vec_fill_overlap<Op, true>), dim3((uint32_t)grid), dim3(kBlock), 0, stream, op);
+    hipLaunchKernelGGL((k_vec_fill_overlap<Op, true>), dim3((uint32_t)grid), dim3(kBlock), lds_pad<Op>(), stream, op);
   else
-    hipLaunchKernelGGL((k_vec_fill_overlap<Op, false>), dim3((uint32_t)grid), dim3(kBlock), 0, stream, op);
+    hipLaunchKernelGGL((k_vec_fill_overlap<Op, false>), dim3((uint32_t)grid), dim3(kBlock), lds_pad<Op>(), stream, op);
   return launch_status();
 }
 
@@ -191,9 +198,9 @@ static tk_status launch_philox_tile(const Op &op, hipStream_t stream) {
   if (grid == 0) grid = 1;
   if (grid > 0x7FFFFFFFull) return TK_EINVAL;
   if (config().nt_stores)
-    hipLaunchKernelGGL((k_philox_tile<Op, true>), dim3((uint32_t)grid), dim3(kBlock), 0, stream, op);
+    hipLaunchKernelGGL((k_philox_tile<Op, true>), dim3((uint32_t)grid), dim3(kBlock), lds_pad<Op>(), stream, op);
   else
-    hipLaunchKernelGGL((k_philox_tile<Op, false>), dim3((uint32_t)grid), dim3(kBlock), 0, stream, op);
+    hipLaunchKernelGGL((k_philox_tile<Op, false>), dim3((uint32_t)grid), dim3(kBlock), lds_pad<Op>(), stream, op);
   return launch_status();
 }
 
@@ -234,9 +241,9 @@ static tk_status launch_pair_tile(const Op &op, hipStream_t stream) {
   if (grid == 0) grid = 1;
   if (grid > 0x7FFFFFFFull) return TK_EINVAL;
   if (config().nt_stores)
-    hipLaunchKernelGGL((k_pair_tile<Op, true>), dim3((uint32_t)grid), dim3(kBlock), 0, stream, op);
+    hipLaunchKernelGGL((k_pair_tile<Op, true>), dim3((uint32_t)grid), dim3(kBlock), lds_pad<Op>(), stream, op);
   else
-    hipLaunchKernelGGL((k_pair_tile<Op, false>), dim3((uint32_t)grid), dim3(kBlock), 0, stream, op);
+    hipLaunchKernelGGL((k_pair_tile<Op, false>), dim3((uint32_t)grid), dim3(kBlock), lds_pad<Op>(), stream, op);
   return launch_status();
 }
 
@@ -263,7 +270,7 @@ static tk_status launch_vec_nt(const Op &op, hipStream_t stream) {
   uint64_t grid = ntiles ? ntiles : 1;
   if (grid > config().max_blocks) grid = config().max_blocks;
   if (grid > 0x7FFFFFFFull) grid = 0x7FFFFFFFull;
-  hipLaunchKernelGGL((k_vec_fill<Op, 1, true>), dim3((uint32_t)grid), dim3(kBlock), 0, stream, op, ntiles);
+  hipLaunchKernelGGL((k_vec_fill<Op, 1, true>), dim3((uint32_t)grid), dim3(kBlock), lds_pad<Op>(), stream, op, ntiles);
   return launch_status();
 }
 
@@ -299,6 +306,7 @@ struct OpConst : FillBase<uint32_t> {
 // u32 / f32: draw i is word i.
 template <bool kFloat>
 struct OpWord32 : FillBase<uint32_t> {
+  static constexpr uint32_t kLdsPad = 32768;
   uint32_t hk;
   __device__ __forceinline__ uint32_t xf(uint32_t w) const { return kFloat ? __float_as_uint(unit23(w)) : w; }
   __device__ __forceinline__ uint32_t elem(uint64_t k) const { return xf(word(hk, (uint32_t)(start + k))); }
@@ -311,6 +319,7 @@ struct OpWord32 : FillBase<uint32_t> {
 // u64 / f64: draw i is words 2i (low) and 2i+1 (high).
 template <bool kFloat>
 struct OpWord64 : FillBase<uint64_t> {
+  static constexpr uint32_t kLdsPad = kFloat ? 24576 : 32768;
   uint32_t hk;
   __device__ __forceinline__ uint64_t xf(uint32_t lo, uint32_t hi) const {
     if (kFloat) return (uint64_t)__double_as_longlong(unit53_lowbits(lo, hi));
@@ -347,6 +356,7 @@ __device__ __forceinline__ uint4 words_at_byte(uint32_t hk, uint32_t w0, uint32_
 // u16 / f16 bits: draw i is half i&1 of word i>>1.
 template <bool kHalf>
 struct OpSub16 : FillBase<uint16_t> {
+  static constexpr uint32_t kLdsPad = kHalf ? 0 : 24576;  // f16: 77.9 -> 82.0 us with a cap
   uint32_t hk;
   __device__ __forceinline__ uint16_t elem(uint64_t k) const {
     const uint64_t i = start + k;
@@ -401,6 +411,7 @@ struct Below32Params {
 // u32 / i32 out, one word per element.
 template <class T>
 struct OpBelow32 : FillBase<T> {
+  static constexpr uint32_t kLdsPad = 32768;
   Below32Params p;
   __device__ __forceinline__ T elem(uint64_t k) const {
     const uint32_t i = (uint32_t)(this->start + k);
@@ -417,6 +428,7 @@ struct OpBelow32 : FillBase<T> {
 
 // i64 out from one word per element: each 16-byte vector holds two elements.
 struct OpBelow32To64 : FillBase<int64_t> {
+  static constexpr uint32_t kLdsPad = 32768;
   Below32Params p;
   __device__ __forceinline__ int64_t elem(uint64_t k) const {
     const uint32_t i = (uint32_t)(start + k);
@@ -434,6 +446,7 @@ struct OpBelow32To64 : FillBase<int64_t> {
 template <class T, bool kSmall>
 struct OpBelow64 : FillBase<T> {
   static constexpr bool kLine = !kSmall;  // the 64-bit products of bounds above 2^32
+  static constexpr uint32_t kLdsPad = kSmall ? 32768 : 0;
   uint32_t hk, hkp;
   uint64_t s, t;
   int64_t low;
@@ -587,9 +600,9 @@ static tk_status launch_exp_t(const Op &op, hipStream_t stream) {
   if (grid == 0) grid = 1;
   if (grid > 0x7FFFFFFFull) return TK_EINVAL;
   if (config().nt_stores)
-    hipLaunchKernelGGL((k_exp_fill<Op, T, true>), dim3((uint32_t)grid), dim3(kBlock), 0, stream, op);
+    hipLaunchKernelGGL((k_exp_fill<Op, T, true>), dim3((uint32_t)grid), dim3(kBlock), lds_pad<Op>(), stream, op);
   else
-    hipLaunchKernelGGL((k_exp_fill<Op, T, false>), dim3((uint32_t)grid), dim3(kBlock), 0, stream, op);
+    hipLaunchKernelGGL((k_exp_fill<Op, T, false>), dim3((uint32_t)grid), dim3(kBlock), lds_pad<Op>(), stream, op);
   return launch_status();
 }
 

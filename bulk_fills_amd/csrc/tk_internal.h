@@ -56,10 +56,20 @@ struct Config {
                                      // tile kernel or the overlapping-wave kernel
   std::atomic<bool> pair_lds;        // TK_PAIRS=lds|wave: Box-Muller pairs at odd starts by the pair tile
                                      // kernel (the next wave's first value through LDS) or each wave alone
+  std::atomic<int> lds_pad;           // TK_LDS_PAD: dynamic LDS bytes per work-group of every streaming fill,
+                                     // which caps the groups resident on a CU (-1, unset: each fill's default)
+  std::atomic<int> zig_lds_pad;       // TK_ZIG_LDS_PAD: the same for the ziggurat table pass
   std::atomic<int> const_work;       // TK_CONST_WORK: dependent integer steps per lane before each store of
                                      // the constant fill (0: none), to sweep the store ceiling's spacing
 };
 const Config &config();
+// The dynamic LDS bytes of a streaming fill's launch: the op's measured default, unless the
+// tunable overrides it.
+template <class Op>
+inline uint32_t lds_pad() {
+  const int v = config().lds_pad;
+  return v >= 0 ? (uint32_t)v : Op::kLdsPad;
+}
 
 // Compute units of the current device (cached per device).
 int device_cus(int device);

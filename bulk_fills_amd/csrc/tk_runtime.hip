@@ -49,6 +49,13 @@ static bool env_tunable(Config &c, const char *name) {
   } else if (!strcmp(name, "pair_lds")) {
     const char *pr = getenv("TK_PAIRS");
     c.pair_lds = !(pr && strcmp(pr, "wave") == 0);
+  } else if (!strcmp(name, "lds_pad")) {
+    const char *lp = getenv("TK_LDS_PAD");
+    const uint64_t b = lp ? env_u64("TK_LDS_PAD", 0) : 0;
+    c.lds_pad = !lp ? -1 : b > 65536 ? 65536 : (int)b;
+  } else if (!strcmp(name, "zig_lds_pad")) {
+    const uint64_t b = env_u64("TK_ZIG_LDS_PAD", 0);
+    c.zig_lds_pad = b > 65536 ? 65536 : (int)b;
   } else if (!strcmp(name, "const_work")) {
     const uint64_t w = env_u64("TK_CONST_WORK", 0);
     c.const_work = w > 4096 ? 4096 : (int)w;
@@ -60,7 +67,7 @@ static bool env_tunable(Config &c, const char *name) {
 
 static const char *const kTunables[] = {"store_nt",  "max_blocks", "unroll",  "choice_tiles", "exp_tiles",
                                         "zig_tiles", "zig_lds",    "zig_fused", "philox_lds", "pair_lds",
-                                        "const_work"};
+                                        "lds_pad",   "zig_lds_pad", "const_work"};
 
 static Config &mutable_config() {
   static Config cfg;
@@ -203,6 +210,8 @@ tk_status tk_debug_set_tunable(const char *name, int64_t value) {
   else if (!strcmp(name, "zig_fused") && one_of({0, 1})) c.zig_fused = value == 1;
   else if (!strcmp(name, "philox_lds") && one_of({0, 1})) c.philox_lds = value == 1;
   else if (!strcmp(name, "pair_lds") && one_of({0, 1})) c.pair_lds = value == 1;
+  else if (!strcmp(name, "lds_pad") && value <= 65536) c.lds_pad = (int)value;
+  else if (!strcmp(name, "zig_lds_pad") && value <= 65536) c.zig_lds_pad = (int)value;
   else if (!strcmp(name, "const_work") && value <= 4096) c.const_work = (int)value;
   else return TK_EINVAL;
   return TK_OK;

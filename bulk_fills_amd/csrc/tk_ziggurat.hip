@@ -546,9 +546,11 @@ static tk_status zig_reserve(ZigDevice &d, uint64_t groups, uint64_t slot_words,
 template <int kB, int T, bool kLds, bool kFused, bool kPhilox>
 static void launch_table_pass(const ZigArgs &a, hipStream_t stream) {
   if (config().nt_stores)
-    hipLaunchKernelGGL((k_zig_table_pass<kB, T, kLds, true, kFused, kPhilox>), dim3(a.ngroups), dim3(kB), 0, stream, a);
+    hipLaunchKernelGGL((k_zig_table_pass<kB, T, kLds, true, kFused, kPhilox>), dim3(a.ngroups), dim3(kB),
+                       (uint32_t)config().zig_lds_pad, stream, a);
   else
-    hipLaunchKernelGGL((k_zig_table_pass<kB, T, kLds, false, kFused, kPhilox>), dim3(a.ngroups), dim3(kB), 0, stream,
+    hipLaunchKernelGGL((k_zig_table_pass<kB, T, kLds, false, kFused, kPhilox>), dim3(a.ngroups), dim3(kB),
+                       (uint32_t)config().zig_lds_pad, stream,
                        a);
 }
 

@@ -219,10 +219,10 @@ def test_tunable_hook_validation():
     value restores the environment's setting (no device involved)."""
     ok = {"store_nt": (0, 1), "max_blocks": (1, 7, (1 << 31) - 1), "unroll": (1, 2, 4),
           "choice_tiles": (1, 2, 4, 8), "exp_tiles": (1, 2, 4), "zig_tiles": (1, 2, 4, 8, 16),
-          "zig_lds": (0, 1), "zig_fused": (0, 1), "philox_lds": (0, 1), "pair_lds": (0, 1),
+          "zig_lds": (0, 1), "zig_fused": (0, 1), "philox_lds": (0, 1), "pair_lds": (0, 1), "lds_pad": (0, 4096, 65536), "zig_lds_pad": (0, 65536),
           "const_work": (0, 1, 4096)}
     bad = {"store_nt": (2,), "max_blocks": (0, 1 << 31), "unroll": (3, 8), "choice_tiles": (3, 16),
-           "exp_tiles": (8,), "zig_tiles": (3, 32), "zig_lds": (2,), "zig_fused": (7,), "philox_lds": (2,), "pair_lds": (2,),
+           "exp_tiles": (8,), "zig_tiles": (3, 32), "zig_lds": (2,), "zig_fused": (7,), "philox_lds": (2,), "pair_lds": (2,), "lds_pad": (65537,), "zig_lds_pad": (65537,),
            "const_work": (4097,)}
     assert set(ok) == set(tk.TUNABLES)
     try:

@@ -145,6 +145,8 @@ CASES = [
     ("const_work", 16, check_constant), ("const_work", 200, check_constant),
     ("philox_lds", 0, check_philox), ("philox_lds", 1, check_philox),
     ("pair_lds", 0, check_pairs), ("pair_lds", 1, check_pairs),
+    ("lds_pad", 0, check_streaming), ("lds_pad", 49152, check_streaming), ("lds_pad", 49152, check_exponential),
+    ("zig_lds_pad", 16384, check_normal_f64),
 ]
 
 
