@@ -190,7 +190,8 @@ __global__ __launch_bounds__(kBlock) void k_choice(ChoiceArgs a) {
 
 template <int T, bool kLds, bool kPhilox>
 static void launch_choice_t(const ChoiceArgs &a, uint32_t grid, hipStream_t stream) {
-  const size_t lds = kLds ? (size_t)((a.n + 1) & ~1u) * sizeof(uint2) : 0;
+  const int pad = config().lds_pad;  // tunable: extra dynamic LDS, which caps the groups per CU
+  const size_t lds = (kLds ? (size_t)((a.n + 1) & ~1u) * sizeof(uint2) : 0) + (pad > 0 ? (size_t)pad : 0);
   if (config().nt_stores)
     hipLaunchKernelGGL((k_choice<T, kLds, true, kPhilox>), dim3(grid), dim3(kBlock), lds, stream, a);
   else

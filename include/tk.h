@@ -286,9 +286,9 @@ tk_status tk_debug_device_bytes(uint64_t *bytes);
  *                         which passes each wave's first value on through LDS (1), or with
  *                         every wave computing the value after it itself (0)
  *                         (TK_PAIRS=lds|wave)
- *   "lds_pad" 0..65536    dynamic LDS bytes allocated per work-group of every streaming fill
- *                         (all but the ziggurat and choice), which caps the groups a compute
- *                         unit holds at once (TK_LDS_PAD; unset: each fill's measured
+ *   "lds_pad" 0..65536    dynamic LDS bytes allocated per work-group of every fill but the
+ *                         ziggurat (for choice, on top of its table), which caps the groups a
+ *                         compute unit holds at once (TK_LDS_PAD; unset: each fill's measured
  *                         default, 24 or 32 KiB for the integer fills, else none)
  *   "zig_lds_pad" 0..65536  the same for the ziggurat table pass (TK_ZIG_LDS_PAD)
  *   "const_work" 0..4096  dependent integer steps per lane before each store of
