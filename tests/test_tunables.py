@@ -146,6 +146,7 @@ CASES = [
     ("philox_lds", 0, check_philox), ("philox_lds", 1, check_philox),
     ("pair_lds", 0, check_pairs), ("pair_lds", 1, check_pairs),
     ("lds_pad", 0, check_streaming), ("lds_pad", 49152, check_streaming), ("lds_pad", 49152, check_exponential),
+    ("lds_pad", 16384, check_choice),
     ("zig_lds_pad", 16384, check_normal_f64),
 ]
 
