@@ -55,6 +55,9 @@ FILL_KERNELS = {
     "exponential_f64": "void tk::k_exp_fill<tk::OpExpF64, 2, false>",
     "exponential_f32": "void tk::k_exp_fill<tk::OpExpF32, 2, false>",
     "calib_copy": "__amd_rocclr_copyBuffer",
+    # store-only references, only when named with --only (2 GiB, one or four tiles per group)
+    "constant_fill": "void tk::k_vec_fill<tk::OpConst, 1, false>",
+    "constant_fill_tiles4": "void tk::k_vec_fill<tk::OpConst, 4, false>",
 }
 # Algorithmic bytes of each fill's 2^28-element launch (written + read) and the sources its
 # kernel is built from (a traffic record holds only while they are unchanged).
@@ -68,7 +71,8 @@ FILL_SOURCES["choice_u32"] = ["bulk_fills_amd/csrc/tk_choice.hip", "bulk_fills_a
 _N28 = 1 << 28
 FILL_BYTES = {"normal_f64": 8 * _N28, "dropout_f32": 8 * _N28, "u64": 8 * _N28, "f64": 8 * _N28, "u32": 4 * _N28,
               "f16_bits": 2 * _N28, "normal_f32": 4 * _N28, "choice_u32": 4 * _N28, "philox_u32": 4 * _N28,
-              "exponential_f64": 8 * _N28, "exponential_f32": 4 * _N28, "calib_copy": 8 * _N28}
+              "exponential_f64": 8 * _N28, "exponential_f32": 4 * _N28, "calib_copy": 8 * _N28,
+              "constant_fill": 8 * _N28, "constant_fill_tiles4": 8 * _N28}
 
 
 def _csv_rows(d, suffix):
@@ -205,7 +209,8 @@ def parse():
                     help="print the per-fill counters of a rocprofv3 --pmc output directory and exit")
     ap.add_argument("--only", default="",
                     help="comma-separated fill names to run (profiling); 'calib_copy' adds a plain 1 GiB "
-                         "device copy used to calibrate the HBM byte counters")
+                         "device copy used to calibrate the HBM byte counters, 'constant_fill' and "
+                         "'constant_fill_tiles4' the 2 GiB store-only fill at one and four tiles per group")
     return ap.parse_args()
 
 
@@ -273,9 +278,18 @@ def build_step(tk, torch, n):
         ("normal_f64_2^20", 8 * m20, 0, zig_kernels, lambda s: tk.tk_fill_normal_f64(1, st(s), m20, optr)),
         ("normal_f64_2^24", 8 * m24, 0, zig_kernels, lambda s: tk.tk_fill_normal_f64(1, st(s), m24, optr)),
     ]
-    # not a fill: a plain copy of a known size, only when named with --only
+    # not fills: a plain copy of a known size and the store-only constant fill at one and four
+    # tiles per group, only when named with --only
     xc = x.view(torch.uint8)
-    calib = ("calib_copy", 4 * n, 4 * n, 1, lambda s: out[:4 * n].copy_(xc))
+    def const_tiles4(s):
+        tk.tk_debug_set_tunable("unroll", 4)
+        try:
+            tk.tk_fill_constant_u32(0, 2 * n, optr)
+        finally:
+            tk.tk_debug_set_tunable("unroll", -1)
+    calib = [("calib_copy", 4 * n, 4 * n, 1, lambda s: out[:4 * n].copy_(xc)),
+             ("constant_fill", 8 * n, 0, 1, lambda s: tk.tk_fill_constant_u32(0, 2 * n, optr)),
+             ("constant_fill_tiles4", 8 * n, 0, 1, const_tiles4)]
 
     # one row per start draw: (fill, start, bytes written, fn)
     def at(fill, nb, f):
@@ -598,7 +612,7 @@ def main():
     fills, next_rows, calib, start_rows, ceil_rows, pattern_rows, keep = build_step(tk, torch, n)
     if args.only:
         wanted = set(args.only.split(","))
-        fills = [f for f in fills + next_rows + [calib] if f[0] in wanted]
+        fills = [f for f in fills + next_rows + calib if f[0] in wanted]
         next_rows, start_rows, ceil_rows, pattern_rows = [], [], [], []
     torch.cuda.synchronize()
 
