@@ -164,13 +164,12 @@ __device__ __forceinline__ void enqueue2(bool p0, bool p1, uint32_t k0, WaveQueu
 template <bool kPhilox>
 __device__ double zig_slow(const ZigArgs &a, uint64_t k);
 
-// One tile: 256 lanes, two elements each.  kCheck guards vectors past the end (only the
-// last group needs it).
-template <bool kAligned4, bool kCheck, bool kFused, bool kNT, bool kPhilox>
-__device__ __forceinline__ void zig_tile(const ZigArgs &a, const double2 *tab, uint64_t v, WaveQueue &wq) {
+// One tile: 256 lanes, two elements each, from the lane's four words.  kCheck guards
+// vectors past the end (only the last group needs it).
+template <bool kCheck, bool kFused, bool kNT>
+__device__ __forceinline__ void zig_tile(const ZigArgs &a, const double2 *tab, uint64_t v, const uint32_t w[4],
+                                         WaveQueue &wq) {
   const bool in = !kCheck || v < a.nvec;
-  uint32_t w[4];
-  zig_words<kAligned4, kPhilox>(a, v, w);
   double y0, y1;
   const bool f0 = zig_fast(tab, w[0], w[1], &y0);
   const bool f1 = zig_fast(tab, w[2], w[3], &y1);
@@ -185,15 +184,34 @@ __device__ __forceinline__ void zig_tile(const ZigArgs &a, const double2 *tab, u
   enqueue2<kFused>(in && !f0, in && !f1, (uint32_t)(a.head + 2 * v), wq, a);
 }
 
-template <int kB, int T, bool kAligned4, bool kFused, bool kNT, bool kPhilox>
-__device__ __forceinline__ void zig_tiles(const ZigArgs &a, const double2 *tab, WaveQueue &wq) {
+// The group's T tiles.  Every lane's words for all of them are hashed first, while the
+// copy of the layer table to LDS (kLds) is still in flight: the loads are issued, the hashes
+// run, and only then does the lane wait for the loads, write LDS and meet the barrier.
+template <int kB, int T, bool kLds, bool kAligned4, bool kFused, bool kNT, bool kPhilox>
+__device__ __forceinline__ void zig_tiles(const ZigArgs &a, double2 *lds_tab, WaveQueue &wq) {
   const uint64_t v0 = (uint64_t)blockIdx.x * T * kB + threadIdx.x;
-  if ((uint64_t)(blockIdx.x + 1) * T * kB <= a.nvec) {
-    for (int t = 0; t < T; ++t)
-      zig_tile<kAligned4, false, kFused, kNT, kPhilox>(a, tab, v0 + (uint64_t)t * kB, wq);
+  uint32_t w[T][4];
+  if (kLds) {
+    constexpr int kPer = 1024 / kB;
+    double2 t[kPer];
+#pragma unroll
+    for (int r = 0; r < kPer; ++r) t[r] = a.xx[threadIdx.x + r * kB];
+#pragma unroll
+    for (int i = 0; i < T; ++i) zig_words<kAligned4, kPhilox>(a, v0 + (uint64_t)i * kB, w[i]);
+#pragma unroll
+    for (int r = 0; r < kPer; ++r) lds_tab[threadIdx.x + r * kB] = t[r];
+    __syncthreads();
   } else {
-    for (int t = 0; t < T; ++t)
-      zig_tile<kAligned4, true, kFused, kNT, kPhilox>(a, tab, v0 + (uint64_t)t * kB, wq);
+#pragma unroll
+    for (int i = 0; i < T; ++i) zig_words<kAligned4, kPhilox>(a, v0 + (uint64_t)i * kB, w[i]);
+  }
+  const double2 *tab = kLds ? lds_tab : a.xx;
+  if ((uint64_t)(blockIdx.x + 1) * T * kB <= a.nvec) {
+#pragma unroll
+    for (int i = 0; i < T; ++i) zig_tile<false, kFused, kNT>(a, tab, v0 + (uint64_t)i * kB, w[i], wq);
+  } else {
+#pragma unroll
+    for (int i = 0; i < T; ++i) zig_tile<true, kFused, kNT>(a, tab, v0 + (uint64_t)i * kB, w[i], wq);
   }
 }
 
@@ -215,23 +233,16 @@ __global__ __launch_bounds__(kB) void k_zig_table_pass(ZigArgs a) {
   __shared__ double2 lds_tab[kLds ? 1024 : 1];
   __shared__ uint32_t q[kWaves * kRegion];
   __shared__ uint32_t wave_n[kWaves];
-  if (kLds) {  // all loads first, then all LDS writes: one L2 round trip per group
-    constexpr int kPer = 1024 / kB;
-    double2 t[kPer];
-#pragma unroll
-    for (int r = 0; r < kPer; ++r) t[r] = a.xx[threadIdx.x + r * kB];
-#pragma unroll
-    for (int r = 0; r < kPer; ++r) lds_tab[threadIdx.x + r * kB] = t[r];
-    __syncthreads();
-  }
   const uint32_t w = threadIdx.x >> 6;
   // entries a wave keeps: its share of the group's slot capacity (smaller when a test
   // shrinks the slots), plus the edge element in the fused pass
   const uint32_t share = (a.slot_cap + kWaves - 1) / kWaves;
   WaveQueue wq{q + w * kRegion, (share < kPerWave ? share : kPerWave) + (kFused ? 1u : 0u), 0u};
+  // (start + head) & 1 is the same for the whole grid: every thread meets the barrier in
+  // zig_tiles on the same branch
+  if (((a.start + a.head) & 1u) == 0) zig_tiles<kB, T, kLds, true, kFused, kNT, kPhilox>(a, lds_tab, wq);
+  else zig_tiles<kB, T, kLds, false, kFused, kNT, kPhilox>(a, lds_tab, wq);
   const double2 *tab = kLds ? lds_tab : a.xx;
-  if (((a.start + a.head) & 1u) == 0) zig_tiles<kB, T, true, kFused, kNT, kPhilox>(a, tab, wq);
-  else zig_tiles<kB, T, false, kFused, kNT, kPhilox>(a, tab, wq);
   if (blockIdx.x == 0) {  // the element before the first boundary and the one after the last vector
     const uint32_t t = threadIdx.x;
     bool edge = false;
