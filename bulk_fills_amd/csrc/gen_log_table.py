@@ -86,7 +86,8 @@ def build():
             a, b = d_interval(j)
             v0 = round_sig(2 / (a + b), D_VBITS)
             q0 = quantum(v0, D_VBITS)
-            v = min((v0 + d * q0 for d in range(-2, 3)), key=lambda c: (d_max_q(j, c), c))
+            cands = [c for c in (v0 + d * q0 for d in range(-2, 3)) if round_sig(c, D_VBITS) == c]
+            v = min(cands, key=lambda c: (d_max_q(j, c), c))
         assert d_max_q(j, v) < Fraction(1, 256), j
         m = v / 2 if j >= D_SPLIT else v
         mf = float(m)
