@@ -543,6 +543,56 @@ def device_info():
             "hip_runtime_version": hip_rt, "torch": torch.__version__, "torch_hip": torch.version.hip}
 
 
+class ClockSampler:
+    """Samples the GPU's shader and memory clocks with `rocm-smi --showclocks --json` (a child
+    process, read-only) every `period` seconds while the per-fill rows run, so the line
+    records the clocks the fills ran at.  Leaves `result` None when rocm-smi is unavailable."""
+
+    def __init__(self, period=0.5):
+        import threading
+        self.period, self.samples, self.result = period, {"sclk": [], "mclk": []}, None
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    def _sample(self):
+        import re
+        import subprocess
+        try:
+            out = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True,
+                                 timeout=10).stdout
+            data = json.loads(out)
+        except Exception:
+            return False
+        card = next(iter(data.values()), {}) if isinstance(data, dict) else {}
+        for key, val in card.items():
+            for clk in ("sclk", "mclk"):
+                if key.lower().startswith(clk):
+                    m = re.search(r"(\d+)\s*mhz", str(val), re.I)
+                    if m:
+                        self.samples[clk].append(int(m.group(1)))
+        return True
+
+    def _run(self):
+        while not self._stop.is_set():
+            if not self._sample():
+                return
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        self._thread.join(timeout=15)
+        res = {}
+        for clk, v in self.samples.items():
+            if v:
+                res[f"{clk}_mhz"] = {"min": min(v), "median": statistics.median(v), "max": max(v), "samples": len(v)}
+        self.result = res or None
+        return False
+
+
 class RowTimer:
     """Times launches of one row: a warm-up of at least `warm_s` seconds, then `k` launches
     each between a pair of fence-free events recorded on the launch stream (back to back:
@@ -670,12 +720,14 @@ def main():
         return rec
 
     # per-fill pass, outside the timed region: warm-up, then 21 event-timed launches per row
+    # (the clocks are sampled meanwhile)
     per_fill = {}
-    for name, wbytes, rbytes, nk, fn in fills:
-        t = rt.time(fn, warm)
-        progress(f"{name}: {t['median_ms'] * 1e3:.1f} us")
-        per_fill[name] = dict(row_record(wbytes, rbytes, t), bytes_written=wbytes, bytes_read=rbytes, kernels=nk,
-                              _median_ms=t["median_ms"])
+    with ClockSampler() as clocks:
+        for name, wbytes, rbytes, nk, fn in fills:
+            t = rt.time(fn, warm)
+            progress(f"{name}: {t['median_ms'] * 1e3:.1f} us")
+            per_fill[name] = dict(row_record(wbytes, rbytes, t), bytes_written=wbytes, bytes_read=rbytes, kernels=nk,
+                                  _median_ms=t["median_ms"])
     # dominant single-kernel fill: the largest share of the step's device time
     single = {k: v for k, v in per_fill.items() if v["kernels"] == 1 and k != "calib_copy"}
     dom = max(single, key=lambda k: single[k]["_median_ms"])
@@ -754,7 +806,7 @@ def main():
         "per_start": per_start,
         "store_pattern": store_pattern,
         "next_rows": nxt,
-        "device": device_info(),
+        "device": dict(device_info(), clocks_during_fill_rows=clocks.result),
     }
     print(json.dumps(rec), flush=True)
     del keep
