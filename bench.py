@@ -781,8 +781,10 @@ def main():
                                "median_us": round(r["median_ms"] * 1e3, 2), "min_us": round(r["min_ms"] * 1e3, 2)}
         progress(f"store pattern {name}: {store_pattern[name]['median_us']} us")
 
-    progress("CPU oracle baseline")
-    cpu = None if args.no_cpu else cpu_baseline(n, args.cpu_single_log2)
+    cpu = None
+    if not args.no_cpu:
+        progress("CPU oracle baseline")
+        cpu = cpu_baseline(n, args.cpu_single_log2)
 
     for v in per_fill.values():
         del v["_median_ms"]
