@@ -544,36 +544,35 @@ def device_info():
 
 
 class ClockSampler:
-    """Samples the GPU's shader and memory clocks with `rocm-smi --showclocks --json` (a child
-    process, read-only) every `period` seconds while the per-fill rows run, so the line
-    records the clocks the fills ran at.  Leaves `result` None when rocm-smi is unavailable."""
+    """Samples the GPU's shader and memory clocks every `period` seconds while the per-fill
+    rows run, so the line records the clocks the fills ran at.  Reads the driver's
+    pp_dpm_sclk / pp_dpm_mclk files under /sys/class/drm (the line marked '*' is the current
+    level; file reads only, no child process).  Leaves `result` None when they are absent."""
 
-    def __init__(self, period=0.5):
+    def __init__(self, period=0.25):
+        import glob
         import threading
         self.period, self.samples, self.result = period, {"sclk": [], "mclk": []}, None
+        cards = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+        self.dev = os.path.dirname(cards[0]) if cards else None
         self._stop = threading.Event()
         self._thread = threading.Thread(target=self._run, daemon=True)
 
     def _sample(self):
         import re
-        import subprocess
-        try:
-            out = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True,
-                                 timeout=10).stdout
-            data = json.loads(out)
-        except Exception:
-            return False
-        card = next(iter(data.values()), {}) if isinstance(data, dict) else {}
-        for key, val in card.items():
-            for clk in ("sclk", "mclk"):
-                if key.lower().startswith(clk):
-                    m = re.search(r"(\d+)\s*mhz", str(val), re.I)
-                    if m:
-                        self.samples[clk].append(int(m.group(1)))
+        for clk in ("sclk", "mclk"):
+            try:
+                lines = open(os.path.join(self.dev, f"pp_dpm_{clk}")).read().splitlines()
+            except OSError:
+                return False
+            for line in lines:
+                m = re.search(r"(\d+)\s*mhz\s*\*", line, re.I)
+                if m:
+                    self.samples[clk].append(int(m.group(1)))
         return True
 
     def _run(self):
-        while not self._stop.is_set():
+        while self.dev and not self._stop.is_set():
             if not self._sample():
                 return
             self._stop.wait(self.period)
@@ -584,7 +583,7 @@ class ClockSampler:
 
     def __exit__(self, *exc):
         self._stop.set()
-        self._thread.join(timeout=15)
+        self._thread.join(timeout=5)
         res = {}
         for clk, v in self.samples.items():
             if v:
