@@ -84,8 +84,9 @@ __device__ __forceinline__ double neg_ln_draw53(uint32_t lo, uint32_t hi, const 
 // the halved entries, so z itself never changes.  Then
 //     -ln x = n ln 2 + ln v_j - ln(1 + q),   ln(1 + q) = q (1 - q/2 + q^2/3 - q^3/4),
 // |q| <= 2^-9 (2^-8 at j = 0), n = 24 - e (23 - e for the halved entries), evaluated as
-// fma(-q, u, w) with u the degree-3 factor and w = n ln 2 + ln v_j: nine f64 operations,
-// where the f64 logarithm above takes seventeen.  n comes from one subtraction: the
+// fma(-q, u, w) with u the degree-3 factor and w = n ln 2 + ln v_j: ten f64 operations
+// (with the conversions and the frexp that takes z / 2 from k), where the f64 logarithm
+// above takes twenty.  n comes from one subtraction: the
 // borrow out of the 20 fraction bits of k's high word is exactly the halving test (fraction
 // bits >= 0x60000).  A CPU model of exactly these operations over all 2^24 inputs (tests)
 // gives the correctly rounded f32 at every one, the worst error being 0.28 of the distance
@@ -107,17 +108,19 @@ __device__ __forceinline__ float neg_ln_grid24_f32(uint32_t m, const LogEntryF *
   const uint32_t j = (xh >> 12) & 0xFFu;
   // 1047 - (xh >> 20), less one when the fraction bits reach 0x60000 (entry 96): 0 <= n <= 24
   const int32_t n = (int32_t)((0x4175FFFFu - xh) >> 20);
-  // z = k 2^-e in [1, 2): k's fraction bits under the exponent of 1, as one v_bitop3
-  // (truth table 0xEA = (a & b) | c)
-  const uint32_t zh = __builtin_amdgcn_bitop3_b32(xh, 0x000FFFFFu, 0x3FF00000u, 0xEA);
-  const double z = __hiloint2double((int)zh, __double2loint(xk));
+  // z / 2 = k 2^-(e+1) in [0.5, 1) in one v_frexp_mant, and h = q / 2 = (z / 2) m - 1/2,
+  // exact as q is.  The polynomial runs on h with its coefficients scaled by powers of two
+  // (8 s, then 4 (s q - 1/2), then 2 u), which gives bit for bit the values of
+  //     s = 1/3 - q/4,  u = 1 + q (s q - 1/2),  -ln x = w - q u
+  // evaluated on q (every step is the same rounding of an exactly scaled value).
+  const double zhalf = __builtin_amdgcn_frexp_mant(xk);
   const LogEntryF t = tab[j];
-  const double q = __builtin_fma(z, t.m, -1.0);  // exact
-  double s = __builtin_fma(-0.25, q, 1.0 / 3);
-  s = __builtin_fma(s, q, -0.5);
-  const double u = __builtin_fma(s, q, 1.0);
+  const double h = __builtin_fma(zhalf, t.m, -0.5);  // exact
+  const double s8 = __builtin_fma(-4.0, h, 8.0 / 3);
+  const double t2 = __builtin_fma(s8, h, -2.0);
+  const double u2 = __builtin_fma(t2, h, 2.0);
   const double w = __builtin_fma((double)n, kLn2, t.l);
-  return (float)__builtin_fma(-q, u, w);
+  return (float)__builtin_fma(-h, u2, w);
 }
 
 }  // namespace tk

@@ -25,16 +25,15 @@ static double model(uint32_t m) {
   const uint32_t xh = (uint32_t)(b >> 32), xl = (uint32_t)b;
   const uint32_t j = (xh >> 12) & 0xFFu;
   const int32_t n = (int32_t)((0x4175FFFFu - xh) >> 20);
-  const uint32_t zh = (xh & 0x000FFFFFu) | 0x3FF00000u;
-  const uint64_t zb = ((uint64_t)zh << 32) | xl;
-  double z;
-  memcpy(&z, &zb, 8);
-  const double q = fma(z, kTab[j][0], -1.0);
-  double s = fma(-0.25, q, 1.0 / 3);
-  s = fma(s, q, -0.5);
-  const double u = fma(s, q, 1.0);
+  (void)xl;
+  int e;
+  const double zhalf = frexp(xk, &e); /* the kernel's v_frexp_mant: z / 2 in [0.5, 1) */
+  const double h = fma(zhalf, kTab[j][0], -0.5);
+  const double s8 = fma(-4.0, h, 8.0 / 3);
+  const double t2 = fma(s8, h, -2.0);
+  const double u2 = fma(t2, h, 2.0);
   const double w = fma((double)n, kLn2, kTab[j][1]);
-  return fma(-q, u, w);
+  return fma(-h, u2, w);
 }
 
 int main(void) {
