@@ -46,32 +46,37 @@ static_assert(TK_LOGD_ENTRIES == 256 && TK_LOGD_SPLIT == 96, "index bits and the
 //    go in last.
 // A CPU model of these operations (tests) finds at most 0.502 ulp of error over every point
 // of the 2^-24 grid and 2^25 more points of the 2^-53 grid, and exact reductions throughout.
-// 20 f64 operations, where the general Tang reduction (z - c_j, a product by 1 / c_j and its
-// residual) with the conversion of u took 27.
+// 21 f64 operations (the frexp that gives z / 2 included) and no integer work for z, where
+// the general Tang reduction (z - c_j, a product by 1 / c_j and its residual) with the
+// conversion of u took 27.
 __device__ __forceinline__ double neg_ln_draw53(uint32_t lo, uint32_t hi, const LogEntryD *tab) {
   const uint32_t b = 0x200000u - (hi & 0x1FFFFFu);
   const double xs = __builtin_fma((double)lo, -0x1p-32, (double)b);  // x 2^21, exact
   const uint32_t xh = (uint32_t)__double2hiint(xs);
   const uint32_t j = (xh >> 12) & 0xFFu;
   const int32_t n = (int32_t)((((1044u << 20) | 0x5FFFFu) - xh) >> 20);
-  // z in [1, 2): x 2^21's fraction bits under the exponent of 1 (v_bitop3 0xEA = (a & b) | c)
-  const uint32_t zh = __builtin_amdgcn_bitop3_b32(xh, 0x000FFFFFu, 0x3FF00000u, 0xEA);
-  const double z = __hiloint2double((int)zh, __double2loint(xs));
+  // z / 2 in [0.5, 1) in one v_frexp_mant, and h = q / 2 = (z / 2) m - 1/2, exact as q is.
+  // Every step below is the step on q with exact power-of-two scalings folded into its
+  // constants (each value is 2^k times the one computed on q, and rounding commutes with the
+  // scaling), so the result is bit for bit that of
+  //     s = -1/2 + q/3 - q^2/4 + q^3/5 - q^4/6 + q^5/7 (Horner),  p = q^2 s,
+  //     rh + rl = w - q (Fast2Sum),  -ln x = rh + (((n LN2_LO + l_lo) - p) + rl).
+  const double zhalf = __builtin_amdgcn_frexp_mant(xs);
   const LogEntryD t = tab[j];
   const double m = __hiloint2double((int)t.m_hi, 0);
   const double l_lo = __hiloint2double((int)t.l_lo_hi, 0);
-  const double q = __builtin_fma(z, m, -1.0);  // exact
-  double s = __builtin_fma(1.0 / 7, q, -1.0 / 6);
-  s = __builtin_fma(s, q, 1.0 / 5);
-  s = __builtin_fma(s, q, -0.25);
-  s = __builtin_fma(s, q, 1.0 / 3);
-  s = __builtin_fma(s, q, -0.5);
-  const double p = (q * q) * s;
+  const double h = __builtin_fma(zhalf, m, -0.5);  // exact
+  double s = __builtin_fma(32 * (1.0 / 7), h, -16 * (1.0 / 6));  // 16 s1
+  s = __builtin_fma(s, h, 8 * (1.0 / 5));                        // 8 s2
+  s = __builtin_fma(s, h, 4 * -0.25);                            // 4 s3
+  s = __builtin_fma(s, h, 2 * (1.0 / 3));                        // 2 s4
+  s = __builtin_fma(s, h, -0.5);                                 // s
+  const double p4 = (h * h) * s;                                 // p / 4
   const double dn = (double)n;
   const double w = __builtin_fma(dn, TK_LN2_HI, t.l_hi);  // exact
-  const double rh = w - q;
-  const double rl = (w - rh) - q;  // exact
-  const double tail = (__builtin_fma(dn, TK_LN2_LO, l_lo) - p) + rl;
+  const double rh = __builtin_fma(h, -2.0, w);            // w - q rounded
+  const double rl = __builtin_fma(h, -2.0, w - rh);       // (w - rh) - q, exact
+  const double tail = __builtin_fma(p4, -4.0, __builtin_fma(dn, TK_LN2_LO, l_lo)) + rl;
   return rh + tail;
 }
 

@@ -39,21 +39,23 @@ static double model(uint32_t lo, uint32_t hi) {
   const uint32_t xh = (uint32_t)(bits >> 32), xl = (uint32_t)bits;
   const uint32_t j = (xh >> 12) & 0xFFu;
   const int32_t n = (int32_t)((((1044u << 20) | 0x5FFFFu) - xh) >> 20);
-  const double z = from_words((xh & 0x000FFFFFu) | 0x3FF00000u, xl);
+  (void)xl;
+  int e;
+  const double zhalf = frexp(xs, &e); /* the kernel's v_frexp_mant: z / 2 in [0.5, 1) */
   const double m = from_words(kTab[j].m_hi, 0), l_lo = from_words(kTab[j].l_lo_hi, 0);
-  const double q = fma(z, m, -1.0);
-  if ((long double)q != (long double)z * (long double)m - 1.0L) ++inexact;
-  double s = fma(1.0 / 7, q, -1.0 / 6);
-  s = fma(s, q, 1.0 / 5);
-  s = fma(s, q, -0.25);
-  s = fma(s, q, 1.0 / 3);
-  s = fma(s, q, -0.5);
-  const double p = (q * q) * s;
+  const double h = fma(zhalf, m, -0.5);
+  if ((long double)h != (long double)zhalf * (long double)m - 0.5L) ++inexact;
+  double s = fma(32 * (1.0 / 7), h, -16 * (1.0 / 6));
+  s = fma(s, h, 8 * (1.0 / 5));
+  s = fma(s, h, 4 * -0.25);
+  s = fma(s, h, 2 * (1.0 / 3));
+  s = fma(s, h, -0.5);
+  const double p4 = (h * h) * s;
   const double dn = (double)n;
   const double w = fma(dn, TK_LN2_HI, kTab[j].l_hi);
-  const double rh = w - q;
-  const double rl = (w - rh) - q;
-  const double tail = (fma(dn, TK_LN2_LO, l_lo) - p) + rl;
+  const double rh = fma(h, -2.0, w);
+  const double rl = fma(h, -2.0, w - rh);
+  const double tail = fma(p4, -4.0, fma(dn, TK_LN2_LO, l_lo)) + rl;
   return rh + tail;
 }
 
