@@ -528,15 +528,16 @@ struct OpRandnF32 : FillBase<float> {
 // ---------------------------------------------------------------------------------------
 // f64: u = (d & (2^53 - 1)) 2^-53 of the 64-bit draw.
 struct OpExpF64 : FillBase<uint64_t> {
-  using Entry = LogEntryD;
+  using Entry = LogEntryWide;  // the LDS copy; the table itself holds LogEntryD
+  static constexpr bool kWiden = true;
   static constexpr int kEntries = TK_LOGD_ENTRIES;
-  __device__ static const Entry *table() { return kLogTableD; }
+  __device__ static const LogEntryD *table() { return kLogTableD; }
   uint32_t hk;
   __device__ __forceinline__ uint64_t elem(uint64_t k) const {
     const uint32_t c = 2u * (uint32_t)(start + k);
     return (uint64_t)__double_as_longlong(neg_ln_draw53(word(hk, c), word(hk, c + 1), kLogTableD));
   }
-  __device__ __forceinline__ uint4 vec(uint64_t v, const LogEntryD *tab) const {
+  __device__ __forceinline__ uint4 vec(uint64_t v, const Entry *tab) const {
     const uint32_t c = 2u * (uint32_t)vec_draw(v);
     const uint64_t a = (uint64_t)__double_as_longlong(neg_ln_draw53(word(hk, c), word(hk, c + 1), tab));
     const uint64_t b = (uint64_t)__double_as_longlong(neg_ln_draw53(word(hk, c + 2), word(hk, c + 3), tab));
@@ -547,6 +548,7 @@ struct OpExpF64 : FillBase<uint64_t> {
 // f32: u = (w & 0xFFFFFF) 2^-24.
 struct OpExpF32 : FillBase<uint32_t> {
   using Entry = LogEntryF;
+  static constexpr bool kWiden = false;
   static constexpr int kEntries = TK_LOGF_ENTRIES;
   __device__ static const Entry *table() { return kLogTableF; }
   uint32_t hk;
@@ -561,26 +563,32 @@ struct OpExpF32 : FillBase<uint32_t> {
 };
 
 // Exponential fills: T 4 KiB tiles per work-group after copying the fill's 4 KiB logarithm
-// table to LDS (16-byte loads, all issued before the LDS writes),
-// so the per-element table reads are ds_reads and not L1 gathers through the texture
-// addresser.
+// table to LDS (16-byte loads, all issued before the LDS writes; the f64 fill widens each
+// entry to three doubles on the way), so the per-element table reads are ds_reads and not
+// L1 gathers through the texture addresser.
 template <class Op, int T, bool kNT>
 __global__ __launch_bounds__(kBlock) void k_exp_fill(Op op) {
   using Entry = typename Op::Entry;
-  constexpr int kPieces = (int)(sizeof(Entry) * Op::kEntries / 16);
-  constexpr int kPer = (kPieces + kBlock - 1) / kBlock;
-  static_assert(sizeof(Entry) * Op::kEntries % 16 == 0, "the table copies in 16-byte pieces");
   __shared__ __align__(16) Entry tab[Op::kEntries];
-  uint4 piece[kPer];
+  if constexpr (Op::kWiden) {  // one entry per lane, widened to whole doubles
+    static_assert(Op::kEntries == kBlock, "one table entry per lane");
+    const LogEntryD e = Op::table()[threadIdx.x];
+    tab[threadIdx.x] = Entry{e.l_hi, log_m(e), log_l_lo(e)};
+  } else {
+    constexpr int kPieces = (int)(sizeof(Entry) * Op::kEntries / 16);
+    constexpr int kPer = (kPieces + kBlock - 1) / kBlock;
+    static_assert(sizeof(Entry) * Op::kEntries % 16 == 0, "the table copies in 16-byte pieces");
+    uint4 piece[kPer];
 #pragma unroll
-  for (int r = 0; r < kPer; ++r) {
-    const int i = (int)threadIdx.x + r * kBlock;
-    if (i < kPieces) piece[r] = ((const uint4 *)Op::table())[i];
-  }
+    for (int r = 0; r < kPer; ++r) {
+      const int i = (int)threadIdx.x + r * kBlock;
+      if (i < kPieces) piece[r] = ((const uint4 *)Op::table())[i];
+    }
 #pragma unroll
-  for (int r = 0; r < kPer; ++r) {
-    const int i = (int)threadIdx.x + r * kBlock;
-    if (i < kPieces) ((uint4 *)tab)[i] = piece[r];
+    for (int r = 0; r < kPer; ++r) {
+      const int i = (int)threadIdx.x + r * kBlock;
+      if (i < kPieces) ((uint4 *)tab)[i] = piece[r];
+    }
   }
   __syncthreads();
   const uint64_t v0 = (uint64_t)blockIdx.x * T * kBlock + threadIdx.x;
