@@ -59,6 +59,13 @@ static double model(uint32_t lo, uint32_t hi) {
   return rh + tail;
 }
 
+#ifdef TK_MODEL_LIB
+/* Library form (tests/build_exp_model.py): the model of each 64-bit draw d, whose low 53
+ * bits are u 2^53, for the GPU test that the fill computes exactly these operations. */
+void tk_model_neg_ln_batch(const uint64_t *d, double *out, size_t n) {
+  for (size_t i = 0; i < n; ++i) out[i] = model((uint32_t)d[i], (uint32_t)(d[i] >> 32));
+}
+#else
 static uint64_t state = 0x9E3779B97F4A7C15ull;
 static uint64_t next(void) {
   state ^= state << 13;
@@ -96,3 +103,4 @@ int main(void) {
   printf("%.6f %ld %ld\n", worst, inexact, wrong_zero);
   return 0;
 }
+#endif

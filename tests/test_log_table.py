@@ -12,11 +12,12 @@ and the f64 one within 0.51 ulp with exact reductions."""
 import os
 import re
 import struct
+import subprocess
+import sys
 from fractions import Fraction
 
-import subprocess
-
 import mpmath as mp
+import numpy as np
 import pytest
 
 CSRC = os.path.join(os.path.dirname(__file__), "..", "bulk_fills_amd", "csrc")
@@ -130,6 +131,29 @@ def parse_f():
     defs = dict(re.findall(r"#define (TK_\w+) (\S+)\n", text))
     rows = [tuple(float.fromhex(v) for v in m) for m in re.findall(r"\{(\S+), (\S+)\}", text)]
     return defs, rows
+
+
+def test_f64_model_library_form():
+    """The library form of the model (tests/libexp_f64_model.so, which the GPU test compares
+    with the fill bit for bit) is the same model: +0 at u = 0, the correctly rounded ln 2
+    at u = 1/2, and within one ulp of numpy's log1p on random 53-bit draws."""
+    import ctypes as C
+    sys.path.insert(0, HERE)
+    import build_exp_model
+    path = build_exp_model.LIB if os.path.exists(build_exp_model.LIB) else build_exp_model.build()
+    lib = C.CDLL(path)
+    lib.tk_model_neg_ln_batch.argtypes = [C.c_void_p, C.c_void_p, C.c_size_t]
+    rng = np.random.default_rng(5)
+    d = rng.integers(0, 1 << 63, 100000, dtype=np.uint64)  # high words carry bits the fill ignores
+    d[:3] = [0, 1 << 52, (1 << 53) - 1]
+    out = np.empty(d.size, dtype=np.float64)
+    lib.tk_model_neg_ln_batch(d.ctypes.data, out.ctypes.data, d.size)
+    assert out[0] == 0.0 and not np.signbit(out[0])
+    assert out[1] == float.fromhex("0x1.62e42fefa39efp-1")
+    u = (d & np.uint64((1 << 53) - 1)).astype(np.float64) * 2.0 ** -53
+    want = -np.log1p(-u)
+    ulp = np.spacing(np.maximum(want, 1e-300))
+    assert np.max(np.abs(out - want) / ulp) <= 1.0
 
 
 def test_f32_table_entries():

@@ -85,6 +85,36 @@ def test_exponential_f64_sweep():
                     assert d.max() <= 2, (key, s, n, off, d.max(), report64(got, want, key, np.arange(n) + s))
 
 
+def _model64():
+    """The host model of the f64 logarithm (tests/exp_f64_model.c, library form, built by
+    build()): the kernel's operations in the same order, IEEE double with explicit fma."""
+    import ctypes as C
+    import os
+    lib = C.CDLL(os.path.join(os.path.dirname(os.path.abspath(__file__)), "libexp_f64_model.so"))
+    lib.tk_model_neg_ln_batch.argtypes = [C.c_void_p, C.c_void_p, C.c_size_t]
+
+    def model(d):
+        d = np.ascontiguousarray(d, dtype=np.uint64)
+        out = np.empty(d.size, dtype=np.float64)
+        lib.tk_model_neg_ln_batch(d.ctypes.data, out.ctypes.data, d.size)
+        return out
+    return model
+
+
+def test_exponential_f64_is_the_modelled_sequence():
+    """Every element of the device's f64 exponential equals the host model of its
+    operations bit for bit (the model's draws are the oracle's 64-bit draws), so the error
+    bound the model establishes on the host (0.502 ulp; tests/test_log_table.py) holds for
+    what the device computes."""
+    model = _model64()
+    n = (1 << 20) + 3
+    for key in (1, 0xFFFFFFFF):
+        for s in (0, 1, 3, (1 << 31) - n):  # the last start ends at the top of the 2^31 draws
+            for off in (0, 1):
+                got = run(tk.tk_fill_exponential_f64, key, s, n, 8, np.float64, off)
+                assert_bits_equal(got, model(oracle.fill_u64(key, s, n)), f"exponential_f64 key={key} s={s} off={off}")
+
+
 def test_exponential_full_size_sampled():
     n = tk_inputs.FULL_N
     idx = tk_inputs.sample_indices(n, seed=18)
